@@ -1,0 +1,245 @@
+"""Python binding of libgqa_decode (GQA decode over a KV cache on MI355X).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libgqa_decode.so``.  torch supplies device memory and the
+current stream.  The names mirror the C ABI in ``include/gqa_decode.h``:
+
+    gqa_decode_make_plan(params)              -> dict
+    gqa_decode_workspace_size(params)         -> int
+    gqa_decode_run(params, q, k_cache, ...)   -> None (writes o, lse)
+    gqa_resolve_rows(params, ..., rows_out)   -> None
+    gqa_status_string(code), gqa_abi_version()
+
+plus ``make_params(...)`` and a convenience ``decode(...)`` that allocates
+the outputs and workspace with torch.  There is no fallback: if the library
+is missing or fails to load, every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgqa_decode.so")
+
+LAYOUT_CONTIGUOUS, LAYOUT_RAGGED, LAYOUT_PAGED = 0, 1, 2
+KV_BF16, KV_FP8_E4M3FN = 0, 1
+GATE_NONE, GATE_ELEMENTWISE, GATE_HEADWISE = 0, 1, 2
+LAYOUTS = {"contiguous": LAYOUT_CONTIGUOUS, "ragged": LAYOUT_RAGGED, "paged": LAYOUT_PAGED}
+KV_DTYPES = {"bf16": KV_BF16, "fp8_e4m3fn": KV_FP8_E4M3FN}
+GATE_MODES = {"none": GATE_NONE, "elementwise": GATE_ELEMENTWISE, "headwise": GATE_HEADWISE}
+
+STATUS = {0: "GQA_OK", 1: "GQA_ERR_INVALID_ARG", 2: "GQA_ERR_UNSUPPORTED", 3: "GQA_ERR_ALIGNMENT",
+          4: "GQA_ERR_WORKSPACE", 5: "GQA_ERR_HIP"}
+
+
+class GqaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class Params(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("s_q", ctypes.c_int32), ("h_q", ctypes.c_int32),
+        ("h_kv", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("layout", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32), ("causal", ctypes.c_int32), ("max_seqlen_kv", ctypes.c_int32),
+        ("seq_capacity", ctypes.c_int32), ("kv_rows", ctypes.c_int64), ("page_size", ctypes.c_int32),
+        ("max_pages_per_seq", ctypes.c_int32), ("topk", ctypes.c_int32), ("gate_mode", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float), ("kv_chunk", ctypes.c_int32), ("num_cus", ctypes.c_int32),
+        ("reserved0", ctypes.c_int32), ("partial_event_begin", ctypes.c_void_p),
+        ("partial_event_end", ctypes.c_void_p),
+    ]
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [
+        ("rows", ctypes.c_int32), ("row_blocks", ctypes.c_int32), ("kv_chunk", ctypes.c_int32),
+        ("num_splits", ctypes.c_int32), ("partial_workgroups", ctypes.c_int64),
+        ("combine", ctypes.c_int32), ("reserved0", ctypes.c_int32), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+_lib_handle = None
+
+
+def load_library(path: Optional[str] = None):
+    """Load libgqa_decode.so (once).  Raises if it is missing."""
+    global _lib_handle
+    if _lib_handle is not None and path is None:
+        return _lib_handle
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"libgqa_decode.so not found at {p}; build it with "
+                           "`python -m gqa_kv_cache_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(p)
+    P = ctypes.POINTER(Params)
+    vp = ctypes.c_void_p
+    lib.gqa_decode_make_plan.argtypes = [P, ctypes.POINTER(Plan)]
+    lib.gqa_decode_workspace_size.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
+    lib.gqa_decode_run.argtypes = [P] + [vp] * 13 + [ctypes.c_size_t, vp]
+    lib.gqa_resolve_rows.argtypes = [P, vp, vp, vp, vp, vp, vp]
+    for f in ("gqa_decode_make_plan", "gqa_decode_workspace_size", "gqa_decode_run", "gqa_resolve_rows"):
+        getattr(lib, f).restype = ctypes.c_int
+    lib.gqa_status_string.argtypes = [ctypes.c_int]
+    lib.gqa_status_string.restype = ctypes.c_char_p
+    lib.gqa_last_error.argtypes = []
+    lib.gqa_last_error.restype = ctypes.c_char_p
+    lib.gqa_abi_version.argtypes = []
+    lib.gqa_abi_version.restype = ctypes.c_int
+    if path is None:
+        _lib_handle = lib
+    return lib
+
+
+def _check(lib, st: int):
+    if st != 0:
+        raise GqaError(st, lib.gqa_last_error().decode())
+
+
+def gqa_abi_version() -> int:
+    return load_library().gqa_abi_version()
+
+
+def gqa_status_string(code: int) -> str:
+    return load_library().gqa_status_string(code).decode()
+
+
+def make_params(*, batch: int, s_q: int, h_q: int, h_kv: int, head_dim: int,
+                layout="contiguous", kv_dtype="bf16", causal: bool = False,
+                max_seqlen_kv: int, seq_capacity: int = 0, kv_rows: int,
+                page_size: int = 16, max_pages_per_seq: int = 0, topk: int = 0,
+                gate_mode="none", softmax_scale: Optional[float] = None,
+                kv_chunk: int = 0, num_cus: int = 0) -> Params:
+    p = Params()
+    p.batch, p.s_q, p.h_q, p.h_kv, p.head_dim = batch, s_q, h_q, h_kv, head_dim
+    p.layout = LAYOUTS[layout] if isinstance(layout, str) else int(layout)
+    p.kv_dtype = KV_DTYPES[kv_dtype] if isinstance(kv_dtype, str) else int(kv_dtype)
+    p.causal = int(bool(causal))
+    p.max_seqlen_kv = max_seqlen_kv
+    p.seq_capacity = seq_capacity
+    p.kv_rows = kv_rows
+    p.page_size = page_size
+    p.max_pages_per_seq = max_pages_per_seq
+    p.topk = topk
+    p.gate_mode = GATE_MODES[gate_mode] if isinstance(gate_mode, str) else int(gate_mode)
+    p.softmax_scale = 0.0 if softmax_scale is None else float(softmax_scale)
+    p.kv_chunk = kv_chunk
+    p.num_cus = num_cus
+    return p
+
+
+def gqa_decode_make_plan(params: Params) -> dict:
+    lib = load_library()
+    plan = Plan()
+    _check(lib, lib.gqa_decode_make_plan(ctypes.byref(params), ctypes.byref(plan)))
+    return {f: getattr(plan, f) for f, _ in Plan._fields_ if not f.startswith("reserved")}
+
+
+def gqa_decode_workspace_size(params: Params) -> int:
+    lib = load_library()
+    n = ctypes.c_size_t(0)
+    _check(lib, lib.gqa_decode_workspace_size(ctypes.byref(params), ctypes.byref(n)))
+    return int(n.value)
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream_handle(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def gqa_decode_run(params: Params, q, k_cache, v_cache, seqlens=None, cu_seqlens=None,
+                   block_table=None, topk_idx=None, k_scale=None, v_scale=None, gate=None,
+                   o=None, lse=None, workspace=None, workspace_bytes: Optional[int] = None,
+                   stream=None) -> None:
+    """Enqueue one decode call.  Tensors are passed by device pointer; the
+    caller keeps them alive until the stream has run the call."""
+    lib = load_library()
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None else (
+            workspace.numel() * workspace.element_size() if not isinstance(workspace, int) else 0)
+    st = lib.gqa_decode_run(ctypes.byref(params), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens),
+                            _ptr(cu_seqlens), _ptr(block_table), _ptr(topk_idx), _ptr(k_scale),
+                            _ptr(v_scale), _ptr(gate), _ptr(o), _ptr(lse), _ptr(workspace),
+                            ctypes.c_size_t(workspace_bytes), _stream_handle(stream))
+    _check(lib, st)
+
+
+def gqa_resolve_rows(params: Params, seqlens=None, cu_seqlens=None, block_table=None,
+                     topk_idx=None, rows_out=None, stream=None) -> None:
+    lib = load_library()
+    st = lib.gqa_resolve_rows(ctypes.byref(params), _ptr(seqlens), _ptr(cu_seqlens), _ptr(block_table),
+                              _ptr(topk_idx), _ptr(rows_out), _stream_handle(stream))
+    _check(lib, st)
+
+
+def decode(q, k_cache, v_cache, *, h_kv: Optional[int] = None, seqlens=None, cu_seqlens=None,
+           block_table=None, topk_idx=None, k_scale=None, v_scale=None, gate=None,
+           gate_mode: Optional[str] = None, causal: bool = False,
+           softmax_scale: Optional[float] = None, max_seqlen_kv: Optional[int] = None,
+           layout: Optional[str] = None, kv_chunk: int = 0, out=None, lse=None, workspace=None,
+           stream=None):
+    """Allocate O / LSE / workspace with torch and run one decode call.
+
+    q: bf16 [B, S_q, H_q, d].  k_cache / v_cache: bf16, or uint8 /
+    float8_e4m3fn codes, as [B, S_cap, H_kv, d] (contiguous),
+    [N, H_kv, d] (ragged, with cu_seqlens) or [pages, P, H_kv, d] (paged,
+    with block_table).  Returns (O bf16 [B, S_q, H_q, d], LSE fp32
+    [B, H_q, S_q]).  ``max_seqlen_kv`` is required for the ragged layout;
+    otherwise it defaults to the cache capacity (no device sync)."""
+    import torch
+
+    B, Sq, Hq, d = q.shape
+    if layout is None:
+        layout = "paged" if block_table is not None else ("ragged" if cu_seqlens is not None else "contiguous")
+    if h_kv is None:
+        h_kv = k_cache.shape[-2]
+    fp8 = k_cache.dtype in (torch.uint8, getattr(torch, "float8_e4m3fn", None))
+    if layout == "contiguous":
+        cap = k_cache.shape[1]
+        kv_rows = k_cache.shape[0] * cap
+        mx = cap if max_seqlen_kv is None else max_seqlen_kv
+        page, mpp = 16, 0
+    elif layout == "ragged":
+        if max_seqlen_kv is None:
+            raise ValueError("ragged layout needs max_seqlen_kv")
+        cap, kv_rows, mx, page, mpp = 0, k_cache.shape[0], max_seqlen_kv, 16, 0
+    else:
+        page = k_cache.shape[1]
+        mpp = block_table.shape[1]
+        cap, kv_rows = 0, k_cache.shape[0] * page
+        mx = mpp * page if max_seqlen_kv is None else max_seqlen_kv
+    if gate_mode is None:
+        gate_mode = "none" if gate is None else ("headwise" if gate.dim() == 3 else "elementwise")
+    params = make_params(batch=B, s_q=Sq, h_q=Hq, h_kv=h_kv, head_dim=d, layout=layout,
+                         kv_dtype="fp8_e4m3fn" if fp8 else "bf16", causal=causal, max_seqlen_kv=mx,
+                         seq_capacity=cap, kv_rows=max(kv_rows, 1), page_size=page,
+                         max_pages_per_seq=mpp,
+                         topk=0 if topk_idx is None else topk_idx.shape[1], gate_mode=gate_mode,
+                         softmax_scale=softmax_scale, kv_chunk=kv_chunk)
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, Sq, Hq, d), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=dev)
+    ws = gqa_decode_workspace_size(params)
+    if ws and workspace is None:
+        workspace = torch.empty(ws, dtype=torch.uint8, device=dev)
+    gqa_decode_run(params, q, k_cache, v_cache, seqlens, cu_seqlens, block_table, topk_idx, k_scale,
+                   v_scale, gate, out, lse, workspace, ws if workspace is not None else 0, stream)
+    return out, lse

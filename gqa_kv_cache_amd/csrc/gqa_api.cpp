@@ -1,0 +1,326 @@
+// C ABI of libgqa_decode: host-side validation, the split planner and the
+// launch sequence (partial kernel, then the LSE combine when the KV walk is
+// split).  No allocation, no device synchronisation.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "gqa_decode.h"
+#include "gqa_device.h"
+
+namespace gqa {
+hipError_t launch_partial(const DecodeArgs& a, int D, bool fp8, bool indirect, int mb, dim3 grid,
+                          hipStream_t st);
+hipError_t launch_combine(const DecodeArgs& a, int D, dim3 grid, hipStream_t st);
+hipError_t launch_resolve(const DecodeArgs& a, int64_t* out, int list_cap, hipStream_t st);
+size_t partial_lds_bytes(int D, bool indirect, int chunk);
+}  // namespace gqa
+
+namespace {
+
+thread_local std::string g_last_error;
+
+gqa_status fail(gqa_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+gqa_status fail(gqa_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+constexpr int kMaxChunkIndirect = 4096;
+constexpr int kMaxRows = 64;
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int log2_exact(int x) {
+  int s = 0;
+  while ((1 << s) < x) ++s;
+  return (1 << s) == x ? s : -1;
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
+
+int device_cus() {
+  static std::mutex mu;
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cached[dev] = cus;
+  }
+  return cached[dev];
+}
+
+// Shape checks shared by every entry point (no pointers looked at).
+gqa_status check_shape(const gqa_decode_params* p) {
+  if (!p) return fail(GQA_ERR_INVALID_ARG, "params is NULL");
+  if (p->batch < 0 || p->batch > 65535) return fail(GQA_ERR_INVALID_ARG, "batch %d outside [0, 65535]", p->batch);
+  if (p->h_q <= 0 || p->h_kv <= 0 || p->h_kv > 65535)
+    return fail(GQA_ERR_INVALID_ARG, "h_q %d / h_kv %d must be positive (h_kv <= 65535)", p->h_q, p->h_kv);
+  if (p->h_q % p->h_kv != 0) return fail(GQA_ERR_INVALID_ARG, "h_q %d is not a multiple of h_kv %d", p->h_q, p->h_kv);
+  if (p->s_q < 1 || p->s_q > 8) return fail(GQA_ERR_UNSUPPORTED, "s_q %d outside [1, 8]", p->s_q);
+  if (p->head_dim != 64 && p->head_dim != 128) return fail(GQA_ERR_UNSUPPORTED, "head_dim %d is not 64 or 128", p->head_dim);
+  const int64_t rows = (int64_t)(p->h_q / p->h_kv) * p->s_q;
+  if (rows > kMaxRows)
+    return fail(GQA_ERR_UNSUPPORTED, "(h_q/h_kv)*s_q = %lld query rows per KV head exceeds %d", (long long)rows, kMaxRows);
+  if (p->layout < GQA_LAYOUT_CONTIGUOUS || p->layout > GQA_LAYOUT_PAGED)
+    return fail(GQA_ERR_INVALID_ARG, "unknown layout %d", p->layout);
+  if (p->kv_dtype != GQA_KV_BF16 && p->kv_dtype != GQA_KV_FP8_E4M3FN)
+    return fail(GQA_ERR_INVALID_ARG, "unknown kv_dtype %d", p->kv_dtype);
+  if (p->gate_mode < GQA_GATE_NONE || p->gate_mode > GQA_GATE_HEADWISE)
+    return fail(GQA_ERR_INVALID_ARG, "unknown gate_mode %d", p->gate_mode);
+  if (p->causal != 0 && p->causal != 1) return fail(GQA_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (p->max_seqlen_kv < 0) return fail(GQA_ERR_INVALID_ARG, "max_seqlen_kv %d < 0", p->max_seqlen_kv);
+  if (p->kv_rows < 1 || p->kv_rows > INT32_MAX)
+    return fail(GQA_ERR_INVALID_ARG, "kv_rows %lld outside [1, 2^31)", (long long)p->kv_rows);
+  if (p->layout == GQA_LAYOUT_CONTIGUOUS) {
+    if (p->seq_capacity < 1 || p->seq_capacity < p->max_seqlen_kv)
+      return fail(GQA_ERR_INVALID_ARG, "seq_capacity %d must be >= max(1, max_seqlen_kv %d)", p->seq_capacity,
+                  p->max_seqlen_kv);
+    if ((int64_t)p->batch * p->seq_capacity > p->kv_rows)
+      return fail(GQA_ERR_INVALID_ARG, "batch * seq_capacity exceeds kv_rows %lld", (long long)p->kv_rows);
+  }
+  if (p->layout == GQA_LAYOUT_PAGED) {
+    if (p->page_size < 1 || p->page_size > 1024 || log2_exact(p->page_size) < 0)
+      return fail(GQA_ERR_UNSUPPORTED, "page_size %d is not a power of two in [1, 1024]", p->page_size);
+    if (p->max_pages_per_seq < 1 || (int64_t)p->max_pages_per_seq * p->page_size < p->max_seqlen_kv)
+      return fail(GQA_ERR_INVALID_ARG, "max_pages_per_seq %d * page_size %d < max_seqlen_kv %d",
+                  p->max_pages_per_seq, p->page_size, p->max_seqlen_kv);
+    if (p->kv_rows % p->page_size != 0)
+      return fail(GQA_ERR_INVALID_ARG, "kv_rows %lld is not a whole number of pages", (long long)p->kv_rows);
+  }
+  if (p->topk < 0) return fail(GQA_ERR_INVALID_ARG, "topk %d < 0", p->topk);
+  if (!std::isfinite(p->softmax_scale)) return fail(GQA_ERR_INVALID_ARG, "softmax_scale is not finite");
+  if (p->kv_chunk != 0) {
+    const bool indirect = p->layout == GQA_LAYOUT_PAGED || p->topk > 0;
+    if (p->kv_chunk < 32 || p->kv_chunk % 32 != 0 || p->kv_chunk > (1 << 24))
+      return fail(GQA_ERR_INVALID_ARG, "kv_chunk %d is not a positive multiple of 32", p->kv_chunk);
+    if (indirect && p->kv_chunk > kMaxChunkIndirect)
+      return fail(GQA_ERR_INVALID_ARG, "kv_chunk %d exceeds %d for paged / top-K lists", p->kv_chunk,
+                  kMaxChunkIndirect);
+  }
+  if (p->num_cus < 0) return fail(GQA_ERR_INVALID_ARG, "num_cus %d < 0", p->num_cus);
+  return GQA_OK;
+}
+
+gqa_status make_plan(const gqa_decode_params* p, gqa_decode_plan* plan) {
+  gqa_status st = check_shape(p);
+  if (st != GQA_OK) return st;
+  std::memset(plan, 0, sizeof *plan);
+  const int rows = (p->h_q / p->h_kv) * p->s_q;
+  plan->rows = rows;
+  plan->row_blocks = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
+  const bool indirect = p->layout == GQA_LAYOUT_PAGED || p->topk > 0;
+  const int64_t L = p->topk > 0 ? p->topk : p->max_seqlen_kv;
+  const int64_t pairs = (int64_t)p->batch * p->h_kv;
+  int64_t chunk = p->kv_chunk;
+  if (chunk == 0) {
+    int cus = p->num_cus ? p->num_cus : device_cus();
+    if (cus <= 0) return fail(GQA_ERR_HIP, "cannot query the device's compute-unit count");
+    // Aim for about four workgroups per CU in total (two resident per CU,
+    // two rounds), with at least 256 and at most 2048 list positions per
+    // workgroup, and never more than the list itself.
+    const int64_t target = 4LL * cus;
+    int64_t per = cdiv(std::max<int64_t>(pairs * L, 1), target);
+    chunk = round_up(std::max<int64_t>(per, 256), 128);
+    chunk = std::min<int64_t>(chunk, 2048);
+    chunk = std::min<int64_t>(chunk, round_up(std::max<int64_t>(L, 1), 32));
+    if (indirect) chunk = std::min<int64_t>(chunk, kMaxChunkIndirect);
+  }
+  const int64_t splits = std::max<int64_t>(1, cdiv(L, chunk));
+  if (splits > INT32_MAX) return fail(GQA_ERR_UNSUPPORTED, "too many splits");
+  plan->kv_chunk = (int32_t)chunk;
+  plan->num_splits = (int32_t)splits;
+  plan->partial_workgroups = pairs * splits;
+  plan->combine = splits > 1 ? 1 : 0;
+  if (splits > 1) {
+    const size_t opart = (size_t)pairs * splits * rows * p->head_dim * sizeof(float);
+    const size_t lpart = (size_t)pairs * splits * rows * sizeof(float);
+    plan->workspace_bytes = round_up(opart, 256) + round_up(lpart, 256);
+  }
+  return GQA_OK;
+}
+
+gqa_status hip_fail(hipError_t e, const char* what) {
+  return fail(GQA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+void fill_args(gqa::DecodeArgs& a, const gqa_decode_params* p, const gqa_decode_plan& plan) {
+  std::memset(&a, 0, sizeof a);
+  a.kv_rows = p->kv_rows;
+  a.batch = p->batch;
+  a.s_q = p->s_q;
+  a.h_q = p->h_q;
+  a.h_kv = p->h_kv;
+  a.group = p->h_q / p->h_kv;
+  a.rows = plan.rows;
+  a.layout = p->layout;
+  a.causal = p->causal;
+  a.max_seqlen = p->max_seqlen_kv;
+  a.seq_cap = p->seq_capacity;
+  a.page_shift = p->layout == GQA_LAYOUT_PAGED ? log2_exact(p->page_size) : 0;
+  a.max_pages = p->max_pages_per_seq;
+  a.topk_len = p->topk;
+  a.gate_mode = p->gate_mode;
+  a.chunk = plan.kv_chunk;
+  a.num_splits = plan.num_splits;
+  const float scale = p->softmax_scale != 0.f ? p->softmax_scale : 1.0f / std::sqrt((float)p->head_dim);
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+}
+
+}  // namespace
+
+extern "C" {
+
+int gqa_abi_version(void) { return GQA_DECODE_ABI_VERSION; }
+
+const char* gqa_last_error(void) { return g_last_error.c_str(); }
+
+const char* gqa_status_string(gqa_status s) {
+  switch (s) {
+    case GQA_OK: return "GQA_OK";
+    case GQA_ERR_INVALID_ARG: return "GQA_ERR_INVALID_ARG";
+    case GQA_ERR_UNSUPPORTED: return "GQA_ERR_UNSUPPORTED";
+    case GQA_ERR_ALIGNMENT: return "GQA_ERR_ALIGNMENT";
+    case GQA_ERR_WORKSPACE: return "GQA_ERR_WORKSPACE";
+    case GQA_ERR_HIP: return "GQA_ERR_HIP";
+  }
+  return "GQA_ERR_UNKNOWN";
+}
+
+gqa_status gqa_decode_make_plan(const gqa_decode_params* p, gqa_decode_plan* plan) {
+  g_last_error.clear();
+  if (!plan) return fail(GQA_ERR_INVALID_ARG, "plan is NULL");
+  return make_plan(p, plan);
+}
+
+gqa_status gqa_decode_workspace_size(const gqa_decode_params* p, size_t* bytes) {
+  g_last_error.clear();
+  if (!bytes) return fail(GQA_ERR_INVALID_ARG, "bytes is NULL");
+  gqa_decode_plan plan;
+  gqa_status st = make_plan(p, &plan);
+  if (st != GQA_OK) return st;
+  *bytes = plan.workspace_bytes;
+  return GQA_OK;
+}
+
+gqa_status gqa_decode_run(const gqa_decode_params* p, const void* q, const void* k_cache,
+                          const void* v_cache, const int32_t* seqlens, const int32_t* cu_seqlens,
+                          const int32_t* block_table, const int32_t* topk_idx, const float* k_scale,
+                          const float* v_scale, const void* gate, void* o, float* lse, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  gqa_decode_plan plan;
+  gqa_status st = make_plan(p, &plan);
+  if (st != GQA_OK) return st;
+  if (!q || !k_cache || !v_cache || !o || !lse) return fail(GQA_ERR_INVALID_ARG, "q, k_cache, v_cache, o and lse are required");
+  if (p->layout == GQA_LAYOUT_RAGGED) {
+    if (!cu_seqlens) return fail(GQA_ERR_INVALID_ARG, "ragged layout needs cu_seqlens");
+  } else if (!seqlens) {
+    return fail(GQA_ERR_INVALID_ARG, "seqlens is required for contiguous and paged layouts");
+  }
+  if (p->layout == GQA_LAYOUT_PAGED && !block_table) return fail(GQA_ERR_INVALID_ARG, "paged layout needs block_table");
+  if (p->topk > 0 && !topk_idx) return fail(GQA_ERR_INVALID_ARG, "topk > 0 needs topk_idx");
+  if (p->kv_dtype == GQA_KV_FP8_E4M3FN && (!k_scale || !v_scale))
+    return fail(GQA_ERR_INVALID_ARG, "FP8 K/V need k_scale and v_scale");
+  if (p->gate_mode != GQA_GATE_NONE && !gate) return fail(GQA_ERR_INVALID_ARG, "gate_mode set but gate is NULL");
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16) ||
+      (p->gate_mode == GQA_GATE_ELEMENTWISE && !aligned(gate, 16)))
+    return fail(GQA_ERR_ALIGNMENT, "q, k_cache, v_cache, o and an elementwise gate must be 16-byte aligned");
+  const void* small[] = {seqlens, cu_seqlens, block_table, topk_idx, k_scale, v_scale, lse, gate};
+  for (const void* ptr : small)
+    if (ptr && !aligned(ptr, 4)) return fail(GQA_ERR_ALIGNMENT, "index, scale, gate and lse arrays must be 4-byte aligned");
+  if (plan.workspace_bytes > 0) {
+    if (!workspace || workspace_bytes < plan.workspace_bytes)
+      return fail(GQA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", plan.workspace_bytes,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned(workspace, 16)) return fail(GQA_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
+  }
+  if (p->batch == 0) return GQA_OK;
+
+  gqa::DecodeArgs a;
+  fill_args(a, p, plan);
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint8_t*>(k_cache);
+  a.v = static_cast<const uint8_t*>(v_cache);
+  a.seqlens = seqlens;
+  a.cu_seqlens = cu_seqlens;
+  a.block_table = block_table;
+  a.topk = topk_idx;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.gate = static_cast<const uint16_t*>(gate);
+  a.o = static_cast<uint16_t*>(o);
+  a.lse = lse;
+  if (plan.workspace_bytes > 0) {
+    const size_t opart = (size_t)p->batch * p->h_kv * plan.num_splits * plan.rows * p->head_dim * sizeof(float);
+    a.o_part = static_cast<float*>(workspace);
+    a.lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + round_up(opart, 256));
+  }
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool indirect = p->layout == GQA_LAYOUT_PAGED || p->topk > 0;
+  const dim3 grid(plan.num_splits, p->h_kv, p->batch);
+  hipError_t e;
+  if (p->partial_event_begin) {
+    e = hipEventRecord(static_cast<hipEvent_t>(p->partial_event_begin), s);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord(begin)");
+  }
+  e = gqa::launch_partial(a, p->head_dim, p->kv_dtype == GQA_KV_FP8_E4M3FN, indirect, plan.row_blocks, grid, s);
+  if (e != hipSuccess) return hip_fail(e, "partial kernel launch");
+  if (p->partial_event_end) {
+    e = hipEventRecord(static_cast<hipEvent_t>(p->partial_event_end), s);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord(end)");
+  }
+  if (plan.combine) {
+    e = gqa::launch_combine(a, p->head_dim, dim3(plan.rows, p->h_kv, p->batch), s);
+    if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
+  }
+  return GQA_OK;
+}
+
+gqa_status gqa_resolve_rows(const gqa_decode_params* p, const int32_t* seqlens, const int32_t* cu_seqlens,
+                            const int32_t* block_table, const int32_t* topk_idx, int64_t* rows_out,
+                            void* stream) {
+  g_last_error.clear();
+  gqa_status st = check_shape(p);
+  if (st != GQA_OK) return st;
+  if (!rows_out) return fail(GQA_ERR_INVALID_ARG, "rows_out is NULL");
+  if (p->layout == GQA_LAYOUT_RAGGED ? !cu_seqlens : !seqlens)
+    return fail(GQA_ERR_INVALID_ARG, "lengths are required (seqlens, or cu_seqlens for ragged)");
+  if (p->layout == GQA_LAYOUT_PAGED && !block_table) return fail(GQA_ERR_INVALID_ARG, "paged layout needs block_table");
+  if (p->topk > 0 && !topk_idx) return fail(GQA_ERR_INVALID_ARG, "topk > 0 needs topk_idx");
+  if (!aligned(rows_out, 8)) return fail(GQA_ERR_ALIGNMENT, "rows_out must be 8-byte aligned");
+  const int list_cap = p->topk > 0 ? p->topk : p->max_seqlen_kv;
+  if (p->batch == 0 || list_cap == 0) return GQA_OK;
+  gqa_decode_plan plan;
+  st = make_plan(p, &plan);
+  if (st != GQA_OK) return st;
+  gqa::DecodeArgs a;
+  fill_args(a, p, plan);
+  a.seqlens = seqlens;
+  a.cu_seqlens = cu_seqlens;
+  a.block_table = block_table;
+  a.topk = topk_idx;
+  hipError_t e = gqa::launch_resolve(a, rows_out, list_cap, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "resolve kernel launch");
+  return GQA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,136 @@
+// Device-side building blocks shared by the decode kernels: argument block,
+// address policies (contiguous / ragged / paged / top-K), wave64 reductions,
+// bf16 and FP8 E4M3FN unpacking, and the MFMA wrapper.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gqa {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kLayoutContiguous = 0;
+constexpr int kLayoutRagged = 1;
+constexpr int kLayoutPaged = 2;
+constexpr int kGateNone = 0;
+constexpr int kGateElementwise = 1;
+constexpr int kGateHeadwise = 2;
+
+constexpr int kThreads = 256;   // 4 wave64s per workgroup
+constexpr int kWaves = 4;
+constexpr int kTile = 32;       // list positions per wave iteration
+
+// Everything a kernel needs, passed by value (kernarg segment).
+struct DecodeArgs {
+  const uint16_t* q;          // bf16 [B, S_q, H_q, D]
+  const uint8_t* k;           // cache bytes (bf16 or fp8)
+  const uint8_t* v;
+  const int32_t* seqlens;     // [B]
+  const int32_t* cu_seqlens;  // [B+1]
+  const int32_t* block_table; // [B, max_pages]
+  const int32_t* topk;        // [B, topk_len]
+  const float* k_scale;       // [B, H_kv]
+  const float* v_scale;
+  const uint16_t* gate;       // bf16
+  uint16_t* o;                // bf16 [B, S_q, H_q, D]
+  float* lse;                 // fp32 [B, H_q, S_q]
+  float* o_part;              // fp32 [B, H_kv, splits, rows, D]
+  float* lse_part;            // fp32 [B, H_kv, splits, rows], base-2
+  int64_t kv_rows;
+  int32_t batch, s_q, h_q, h_kv, group, rows;
+  int32_t layout, causal, max_seqlen, seq_cap;
+  int32_t page_shift, max_pages, topk_len, gate_mode;
+  int32_t chunk, num_splits;
+  float scale_log2;           // softmax scale * log2(e)
+};
+
+// ---------------------------------------------------------------------------
+// Address policy.  A request's list has L entries: its n tokens (dense) or
+// its top-K positions.  Slot p names logical token t; t names a physical
+// token row of the cache.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ int seq_len(const DecodeArgs& a, int b) {
+  int n = (a.layout == kLayoutRagged) ? (a.cu_seqlens[b + 1] - a.cu_seqlens[b]) : a.seqlens[b];
+  return max(0, min(n, a.max_seqlen));
+}
+
+__device__ __forceinline__ int list_len(const DecodeArgs& a, int n) {
+  return a.topk_len > 0 ? a.topk_len : n;
+}
+
+// First token row of request b for the non-paged layouts.
+__device__ __forceinline__ int64_t row_base(const DecodeArgs& a, int b) {
+  if (a.layout == kLayoutContiguous) return (int64_t)b * a.seq_cap;
+  if (a.layout == kLayoutRagged) return (int64_t)a.cu_seqlens[b];
+  return 0;
+}
+
+// Logical token of list slot p (p < L), or -1 if the slot is masked.
+__device__ __forceinline__ int slot_token(const DecodeArgs& a, int b, int n, int p) {
+  int t = (a.topk_len > 0) ? a.topk[(int64_t)b * a.topk_len + p] : p;
+  return (t >= 0 && t < n) ? t : -1;
+}
+
+// Physical token row of logical token t (0 <= t < n) of request b, clamped
+// into the cache so that no offset can address memory outside it.
+__device__ __forceinline__ int64_t token_row(const DecodeArgs& a, int b, int t, int64_t base) {
+  int64_t row;
+  if (a.layout == kLayoutPaged) {
+    const int page = a.block_table[(int64_t)b * a.max_pages + (t >> a.page_shift)];
+    row = ((int64_t)page << a.page_shift) + (t & ((1 << a.page_shift) - 1));
+  } else {
+    row = base + t;
+  }
+  return min(max(row, (int64_t)0), a.kv_rows - 1);
+}
+
+// ---------------------------------------------------------------------------
+// Wave64 helpers
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __builtin_bit_cast(float, u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __builtin_bit_cast(float, u & 0xFFFF0000u); }
+
+// Two floats -> packed bf16 pair, round to nearest even.
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Four FP8 E4M3FN codes (one dword, lowest byte first) -> four bf16 in two
+// dwords.  Every E4M3FN value is exactly representable in bf16.
+__device__ __forceinline__ void fp8x4_to_bf16x4(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+  hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+}
+
+// D(16x16 fp32) += A(16x32 bf16) * B(32x16 bf16).  Lane l holds A row l%16,
+// B column l%16, each for k = 8*(l/16) .. 8*(l/16)+7, and D rows
+// 4*(l/16) .. 4*(l/16)+3 of column l%16.
+__device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
+
+}  // namespace gqa

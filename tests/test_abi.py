@@ -1,0 +1,140 @@
+"""The C-ABI library on the host (no GPU needed): it loads, exports every
+entry point the header declares, and rejects bad arguments with the right
+status before touching a device."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import gqa_kv_cache_amd as G
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "gqa_decode.h")
+
+# Fake, aligned device addresses: validation never dereferences pointers.
+A16 = 0x10000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gqa_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = G.load_library()
+    names = declared_functions()
+    assert {"gqa_decode_run", "gqa_decode_workspace_size", "gqa_decode_make_plan", "gqa_resolve_rows",
+            "gqa_status_string", "gqa_last_error", "gqa_abi_version"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in gqa_decode.h but not exported"
+
+
+def test_binding_argument_counts_match_header():
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    lib = G.load_library()
+    for name in declared_functions():
+        m = re.search(r"\b" + name + r"\s*\((.*?)\)\s*;", text, flags=re.S)
+        args = [a for a in m.group(1).split(",") if a.strip() and a.strip() != "void"]
+        fn = getattr(lib, name)
+        if fn.argtypes is not None:
+            assert len(fn.argtypes) == len(args), f"{name}: binding has {len(fn.argtypes)} args, header {len(args)}"
+
+
+def test_version_and_status_strings():
+    assert G.gqa_abi_version() == 1
+    for code, name in G.STATUS.items():
+        assert G.gqa_status_string(code) == name
+
+
+def base(**kw):
+    d = dict(batch=2, s_q=1, h_q=8, h_kv=2, head_dim=128, max_seqlen_kv=100, seq_capacity=100,
+             kv_rows=200, num_cus=256)
+    d.update(kw)
+    return G.make_params(**d)
+
+
+BAD_SHAPES = [
+    (dict(h_q=6, h_kv=4), 1),
+    (dict(h_kv=0), 1),
+    (dict(s_q=0), 2),
+    (dict(s_q=9), 2),
+    (dict(head_dim=96), 2),
+    (dict(h_q=128, h_kv=1), 2),             # 128 rows per KV head
+    (dict(h_q=16, h_kv=1, s_q=8), 2),       # 128 rows
+    (dict(layout=7), 1),
+    (dict(kv_dtype=3), 1),
+    (dict(gate_mode=5), 1),
+    (dict(max_seqlen_kv=-1), 1),
+    (dict(seq_capacity=50), 1),             # capacity < max length
+    (dict(kv_rows=100), 1),                 # batch * capacity > kv_rows
+    (dict(kv_rows=0), 1),
+    (dict(layout="paged", page_size=12, max_pages_per_seq=10, kv_rows=192), 2),
+    (dict(layout="paged", page_size=16, max_pages_per_seq=2, kv_rows=192), 1),  # 32 < 100
+    (dict(layout="paged", page_size=16, max_pages_per_seq=7, kv_rows=100), 1),  # not whole pages
+    (dict(topk=-1), 1),
+    (dict(kv_chunk=48), 1),
+    (dict(kv_chunk=8192, layout="paged", page_size=16, max_pages_per_seq=7, kv_rows=224), 1),
+    (dict(softmax_scale=float("inf")), 1),
+    (dict(batch=70000), 1),
+]
+
+
+@pytest.mark.parametrize("kw,status", BAD_SHAPES)
+def test_plan_rejects_bad_shapes(kw, status):
+    with pytest.raises(G.GqaError) as e:
+        G.gqa_decode_make_plan(base(**kw))
+    assert e.value.status == status, str(e.value)
+
+
+def test_plan_never_sizes_an_expansion():
+    # the workspace holds split partials only: O(splits * rows * d), never
+    # O(S_kv * H_q * d) as a K/V expansion to the query-head count would
+    p = base(batch=1, h_q=64, h_kv=8, s_q=2, max_seqlen_kv=131072, seq_capacity=131072, kv_rows=131072)
+    plan = G.gqa_decode_make_plan(p)
+    expansion = 2 * 131072 * 64 * 128 * 2
+    assert plan["workspace_bytes"] < expansion / 100
+    assert plan["workspace_bytes"] == G.gqa_decode_workspace_size(p)
+    assert plan["rows"] == 16 and plan["row_blocks"] == 1 and plan["num_splits"] * plan["kv_chunk"] >= 131072
+
+
+def test_plan_forced_chunk_and_single_split():
+    p = base(kv_chunk=32)
+    plan = G.gqa_decode_make_plan(p)
+    assert plan["num_splits"] == 4 and plan["combine"] == 1 and plan["workspace_bytes"] > 0
+    p = base(kv_chunk=128)
+    plan = G.gqa_decode_make_plan(p)
+    assert plan["num_splits"] == 1 and plan["combine"] == 0 and plan["workspace_bytes"] == 0
+
+
+def _run(p, **ptrs):
+    args = dict(q=A16, k=A16, v=A16, seqlens=A16, cu=None, bt=None, topk=None, ks=None, vs=None,
+                gate=None, o=A16, lse=A16, ws=A16, ws_bytes=1 << 30)
+    args.update(ptrs)
+    lib = G.load_library()
+    return lib.gqa_decode_run(ctypes.byref(p), args["q"], args["k"], args["v"], args["seqlens"], args["cu"],
+                              args["bt"], args["topk"], args["ks"], args["vs"], args["gate"], args["o"],
+                              args["lse"], args["ws"], ctypes.c_size_t(args["ws_bytes"]), None)
+
+
+def test_run_validation_statuses():
+    p = base()
+    assert _run(p, q=None) == 1
+    assert _run(p, seqlens=None) == 1
+    assert _run(p, q=A16 + 2) == 3                       # misaligned
+    assert _run(p, lse=A16 + 2) == 3
+    assert _run(base(layout="ragged"), cu=None) == 1
+    assert _run(base(layout="paged", page_size=16, max_pages_per_seq=7, kv_rows=224)) == 1  # no block table
+    assert _run(base(topk=8)) == 1                        # no topk_idx
+    assert _run(base(kv_dtype="fp8_e4m3fn")) == 1          # no scales
+    assert _run(base(gate_mode="elementwise")) == 1        # no gate
+    assert _run(base(gate_mode="elementwise"), gate=A16 + 4) == 3
+    assert _run(base(kv_chunk=32), ws=None) == 4           # workspace needed
+    assert _run(base(kv_chunk=32), ws_bytes=16) == 4
+    msg = G.load_library().gqa_last_error().decode()
+    assert "workspace" in msg
+
+
+def test_run_batch_zero_is_a_no_op():
+    assert _run(base(batch=0, kv_rows=1)) == 0

@@ -1,0 +1,227 @@
+"""Bit-exact checks of the HIP path (needs a gfx950 GPU).
+
+* gqa_resolve_rows (the decode kernels' own address code) against the
+  oracle's resolve_rows: int64, torch.equal.
+* One-hot probes: q and K are set so that one chosen token of each (request,
+  KV head) outscores every other by more than 200 in log2 units; its softmax
+  weight is then exactly 1 and every other weight (and every other split's
+  combine weight) exactly 0 in fp32, so O must equal that token's V row bit
+  for bit.  V rows encode their physical row id in small integers, which
+  bf16 and FP8 represent exactly.  This pins paged / ragged / top-K
+  addressing end to end through the decode kernels, for any split plan.
+* Invariances that must hold bitwise on the device: page-table
+  permutation, paged vs contiguous storage of the same cache, and
+  run-to-run determinism.
+"""
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import gqa_inputs as gi
+import gqa_kv_cache_amd as G
+import oracle.reference as R
+from gpu_common import Uploaded, log
+
+pytestmark = pytest.mark.gpu
+
+
+def spec(**kw):
+    base = dict(name="x", batch=2, h_q=8, h_kv=4, head_dim=128, s_q=1, layout="contiguous")
+    base.update(kw)
+    if "fixed_lengths" in base:
+        base["batch"] = len(base["fixed_lengths"])
+    return gi.Spec(**base)
+
+
+def _oracle_rows(w):
+    s = w.spec
+    cap = w.k_cache.shape[1] if s.layout == "contiguous" else 0
+    return R.resolve_rows(batch=s.batch, s_q=s.s_q, layout=s.layout, seqlens=w.seqlens,
+                          cu_seqlens=w.cu_seqlens, block_table=w.block_table, topk_idx=w.topk_idx,
+                          page_size=s.page_size, capacity=cap, causal=s.causal,
+                          list_len=s.topk if s.topk else w.max_seqlen)
+
+
+RESOLVE_CASES = [
+    spec(layout="contiguous", s_q=3, causal=True, fixed_lengths=(5, 70, 0), capacity=80),
+    spec(layout="ragged", s_q=2, causal=True, fixed_lengths=(6, 0, 41, 1)),
+    spec(layout="paged", page_size=16, fixed_lengths=(300, 17, 0)),
+    spec(layout="paged", page_size=4, s_q=4, causal=True, fixed_lengths=(9, 14, 3)),
+    spec(layout="paged", page_size=16, topk=64, topk_mode="random_masked", s_q=2, causal=True,
+         fixed_lengths=(60, 5, 0)),
+    spec(layout="ragged", topk=33, topk_mode="random_masked", fixed_lengths=(30, 2)),
+]
+
+
+@pytest.mark.parametrize("idx", range(len(RESOLVE_CASES)))
+def test_resolve_rows_bit_exact(idx):
+    w = gi.build(RESOLVE_CASES[idx], seed=100 + idx)
+    up = Uploaded(w)
+    want = _oracle_rows(w)
+    out = torch.full(want.shape, -7, dtype=torch.int64, device="cuda")
+    G.gqa_resolve_rows(up.params, up.seqlens, up.cu, up.bt, up.topk, out)
+    got = out.cpu()
+    assert torch.equal(got, torch.from_numpy(want)), f"case {idx}: {(got.numpy() != want).sum()} slots differ"
+
+
+def _probe(w, rng, fp8=False):
+    """Rewrite q, K, V of a workload into a one-hot probe.  Returns the
+    expected O (bf16 bits or FP8 codes of the target V rows)."""
+    s = w.spec
+    B, Sq, Hq, Hkv, d = s.batch, s.s_q, s.h_q, s.h_kv, s.head_dim
+    G_ = Hq // Hkv
+    rows = _oracle_rows(w)                     # [B, S_q, L]
+    kf = w.k_cache.reshape(-1, Hkv, d)
+    vf = w.v_cache.reshape(-1, Hkv, d)
+    if fp8:
+        one, big = 0x4100, 0x7E                # q = bf16 8.0, K = E4M3FN 448.0
+        kf[:, :, 0] = 0
+    else:
+        one, big = 0x3F80, 0x4500              # bf16 1.0 and 2048.0
+        kf[:, :, 0] = 0
+    w.q[...] = 0
+    w.q[..., 0] = one
+    # V[row, g, :] encodes (row, g) in base-16 (FP8) or base-256 (bf16) digits
+    nrow = vf.shape[0]
+    rid = np.arange(nrow, dtype=np.int64)
+    base = 16 if fp8 else 256
+    digits = np.zeros((nrow, Hkv, d), dtype=np.int64)
+    for c in range(d):
+        if c < 4:
+            digits[:, :, c] = (rid[:, None] // base ** c) % base
+        elif c == 4:
+            digits[:, :, c] = np.arange(Hkv)[None, :] % base
+        else:
+            digits[:, :, c] = (rid[:, None] * 7 + c + np.arange(Hkv)[None, :]) % base
+    if fp8:
+        codes = torch.from_numpy(digits.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        vf[...] = codes
+    else:
+        vf[...] = gi.f32_to_bf16_bits(digits.astype(np.float32))
+    expect = {}
+    for b in range(B):
+        for g in range(Hkv):
+            vis0 = np.nonzero(rows[b, 0] >= 0)[0]   # slots visible to query 0 are visible to all
+            if vis0.size == 0:
+                continue
+            slot = int(rng.choice(vis0))
+            target = int(rows[b, 0, slot])
+            kf[target, g, 0] = big
+            expect[(b, g)] = target
+    if fp8:
+        w.k_scale[...] = 1.0
+        w.v_scale[...] = 1.0
+    return expect
+
+
+PROBE_CASES = [
+    ("contiguous", spec(layout="contiguous", h_q=64, h_kv=8, s_q=2, causal=True, fixed_lengths=(3000, 40), capacity=3100), False),
+    ("ragged", spec(layout="ragged", h_q=32, h_kv=8, fixed_lengths=(700, 1, 0, 2049)), False),
+    ("paged", spec(layout="paged", h_q=64, h_kv=8, page_size=16, fixed_lengths=(1500, 33)), False),
+    ("sparse", spec(layout="paged", h_q=32, h_kv=8, page_size=16, topk=300, topk_mode="random_masked", fixed_lengths=(250, 400)), False),
+    ("fp8_sparse", spec(layout="paged", h_q=32, h_kv=8, page_size=16, topk=512, topk_mode="permutation",
+                        kv_dtype="fp8_e4m3fn", fixed_lengths=(512, 512, 512)), True),
+]
+
+
+@pytest.mark.parametrize("name,s,fp8", PROBE_CASES, ids=[c[0] for c in PROBE_CASES])
+@pytest.mark.parametrize("chunk", [0, 32, 96])
+def test_one_hot_probe(name, s, fp8, chunk):
+    w = gi.build(s, seed=7)
+    rng = np.random.default_rng(chunk + 1)
+    expect = _probe(w, rng, fp8=fp8)
+    up = Uploaded(w, kv_chunk=chunk)
+    up.run()
+    torch.cuda.synchronize()
+    O = up.o.view(torch.int16).cpu().numpy().view(np.uint16)
+    Hkv, d = s.h_kv, s.head_dim
+    Gq = s.h_q // Hkv
+    vf = w.v_cache.reshape(-1, Hkv, d)
+    checked = 0
+    for (b, g), target in expect.items():
+        want = vf[target, g]
+        if fp8:   # O is bf16: the decoded FP8 integer digits are exact in bf16
+            want = gi.f32_to_bf16_bits(torch.from_numpy(want).view(torch.float8_e4m3fn).float().numpy())
+        for i in range(s.s_q):
+            for h in range(g * Gq, (g + 1) * Gq):
+                assert np.array_equal(O[b, i, h], want), f"{name}: (b={b}, i={i}, h={h}) expected row {target}"
+                checked += 1
+    log(f"  probe {name} chunk={chunk}: {checked} rows exact")
+    assert checked > 0
+
+
+def _run_bits(w, chunk=0):
+    up = Uploaded(w, kv_chunk=chunk)
+    up.run()
+    torch.cuda.synchronize()
+    return up.o.view(torch.int16).cpu().clone(), up.lse.cpu().clone()
+
+
+def test_page_permutation_bitwise():
+    s = spec(layout="paged", h_q=64, h_kv=8, page_size=16, fixed_lengths=(900, 77))
+    w = gi.build(s, seed=12)
+    o1, l1 = _run_bits(w)
+    pool = w.k_cache.shape[0]
+    perm = np.random.default_rng(3).permutation(pool)
+    k2 = np.empty_like(w.k_cache); k2[perm] = w.k_cache
+    v2 = np.empty_like(w.v_cache); v2[perm] = w.v_cache
+    w2 = dataclasses.replace(w, k_cache=k2, v_cache=v2, block_table=perm[w.block_table].astype(np.int32))
+    o2, l2 = _run_bits(w2)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_paged_equals_contiguous_bitwise():
+    n = 1000
+    s = spec(layout="contiguous", h_q=32, h_kv=8, fixed_lengths=(n, n))
+    wc = gi.build(s, seed=13)
+    P = 16
+    pages = -(-n // P)
+    B = 2
+    bt = np.arange(B * pages, dtype=np.int32).reshape(B, pages)
+    kp = np.zeros((B * pages, P, 8, 128), dtype=np.uint16)
+    vp = np.zeros_like(kp)
+    for b in range(B):
+        kp.reshape(B, pages * P, 8, 128)[b, :n] = wc.k_cache[b, :n]
+        vp.reshape(B, pages * P, 8, 128)[b, :n] = wc.v_cache[b, :n]
+    wp = dataclasses.replace(wc, spec=dataclasses.replace(s, layout="paged", page_size=P), k_cache=kp,
+                             v_cache=vp, block_table=bt)
+    for chunk in (0, 128):
+        oc, lc = _run_bits(wc, chunk)
+        op, lp = _run_bits(wp, chunk)
+        assert torch.equal(oc, op) and torch.equal(lc, lp), f"chunk {chunk}"
+
+
+def test_run_to_run_deterministic():
+    s = spec(layout="ragged", h_q=64, h_kv=8, s_q=2, causal=True, fixed_lengths=(5000, 123, 2048))
+    w = gi.build(s, seed=14)
+    up = Uploaded(w, kv_chunk=256)
+    outs = []
+    for _ in range(10):
+        up.o.fill_(0)
+        up.lse.fill_(0)
+        up.run()
+        torch.cuda.synchronize()
+        outs.append((up.o.view(torch.int16).cpu().clone(), up.lse.cpu().clone()))
+    for o, l in outs[1:]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(l, outs[0][1])
+
+
+def test_outputs_written_in_full():
+    # NaN-prefilled outputs must be overwritten everywhere, including rows
+    # with nothing visible.
+    s = spec(layout="ragged", h_q=16, h_kv=4, s_q=3, causal=True, fixed_lengths=(0, 2, 50))
+    w = gi.build(s, seed=15)
+    for chunk in (0, 32):
+        up = Uploaded(w, kv_chunk=chunk)
+        up.o.fill_(float("nan"))
+        up.lse.fill_(float("nan"))
+        up.run()
+        torch.cuda.synchronize()
+        assert not torch.isnan(up.o.float()).any() and not torch.isnan(up.lse).any()
+        lse = up.lse.cpu().numpy()
+        assert np.isneginf(lse[0]).all()             # empty request
+        assert np.isneginf(lse[1, :, 0])             .all()  # n=2, s_q=3: query 0 sees nothing
+        assert (up.o[0].float() == 0).all()
