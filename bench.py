@@ -1,0 +1,295 @@
+#!/usr/bin/env python3
+"""Benchmark of GQA decode over a KV cache on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long128k]
+
+A step is one decode call (split-KV partial kernel + LSE combine) over the
+resident synthetic inputs of the workload.  The default workload is the
+long-context decode: batch 1, 64 query / 8 KV heads, d=128, S_q=2 causal,
+a 128K-token bf16 cache (512 MiB of K+V) — the shape of the results table
+in "When the K/V copy costs more than the attention".
+
+Prints one JSON line: achieved bandwidth over the minimum bytes a call must
+move (K/V + Q + O + LSE + lengths) divided by the measured time per call,
+the roofline of the partial kernel (algorithmic K/V bytes per launch over
+its event-timed duration, against 8 TB/s), and the CPU oracle timed on a
+bounded sample of the same workload.  Progress goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "µs/call and achieved HBM GB/s (% of peak), GQA decode 64/8 d128 128K KV"
+HBM_PEAK_GBPS = 8000.0
+KERNEL_SOURCES = ["gqa_kv_cache_amd/csrc/gqa_kernels.hip", "gqa_kv_cache_amd/csrc/gqa_device.h"]
+
+
+def say(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str):
+    """HBM bytes per partial-kernel launch from the committed rocprofv3
+    counter summary, or None if absent or taken on other kernel source."""
+    path = os.path.join(ROOT, "profiles", f"gqa_partial_kernel_{workload}_pmc.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    try:
+        if kv.get("kernel_source_sha256") != kernel_source_hash():
+            return None
+        fetch = float(kv["FETCH_SIZE_KiB_per_dispatch"]) * float(kv["fetch_scale"])
+        write = float(kv["WRITE_SIZE_KiB_per_dispatch"]) * float(kv["write_scale"])
+        return (fetch + write) * 1024.0
+    except (KeyError, ValueError):
+        return None
+
+
+def workload_bytes(w):
+    """(minimum bytes per call, algorithmic K/V bytes per partial launch)."""
+    from gqa_kv_cache_amd import costs
+    s = w.spec
+    es = 1 if s.kv_dtype == "fp8_e4m3fn" else 2
+    if s.topk:
+        tokens = sum(len(set(int(t) for t in w.topk_idx[b] if 0 <= t < w.seqlens[b])) for b in range(s.batch))
+    else:
+        tokens = int(w.seqlens.astype("int64").sum())
+    pages = 0
+    if s.layout == "paged":
+        pages = sum(-(-int(n) // s.page_size) for n in w.seqlens)
+    mb = costs.minimum_bytes(batch=s.batch, s_q=s.s_q, h_q=s.h_q, h_kv=s.h_kv, d=s.head_dim,
+                             kv_elem_bytes=es, tokens=tokens, layout=s.layout, pages_touched=pages,
+                             topk=s.topk, fp8_scales=s.kv_dtype == "fp8_e4m3fn", gate=w.gate is not None)
+    kv = 2 * tokens * s.h_kv * s.head_dim * es
+    return mb, kv, tokens
+
+
+def cpu_baseline(w, min_bytes, budget_s=10.0):
+    """The fp64 oracle on whole KV heads of the same workload (one BLAS
+    thread), KV head by KV head until ``budget_s`` is used; throughput is
+    scaled to the sampled share of the minimum bytes."""
+    import oracle.reference as R
+    from threadpoolctl import threadpool_limits
+    s = w.spec
+    G = s.h_q // s.h_kv
+    t0 = time.perf_counter()
+    heads = 0
+    with threadpool_limits(1):
+        for g in range(s.h_kv):
+            rows = [(b, i, h) for b in range(s.batch) for i in range(s.s_q) for h in range(g * G, (g + 1) * G)]
+            R.reference_decode(**w.arrays(), **w.params(), rows=rows)
+            heads += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+    dt = time.perf_counter() - t0
+    frac = heads / s.h_kv
+    return {"value": round(min_bytes * frac / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{heads} of {s.h_kv} KV heads ({heads * G * s.s_q * s.batch} of "
+                      f"{s.h_q * s.s_q * s.batch} query rows), {dt:.1f} s on "
+                      f"{platform.processor() or platform.machine()}",
+            "seconds": round(dt, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="long128k",
+                    choices=["tiny", "long128k", "ragged", "ragged_sq8", "paged", "sparse_fp8"])
+    ap.add_argument("--kv-chunk", type=int, default=0, help="force list positions per workgroup")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold", action="store_true", help="also time single calls after a 1 GiB cache flush")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run and time a 512 MiB device-to-device copy (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the decode path has no multi-GPU mode in this build", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gqa_inputs as gi
+    import gqa_kv_cache_amd as G
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    G.load_library()
+
+    say(f"generating workload {args.workload}")
+    t = time.perf_counter()
+    w = gi.named(args.workload)
+    s = w.spec
+    say(f"  generated in {time.perf_counter() - t:.1f} s")
+    min_bytes, kv_bytes, tokens = workload_bytes(w)
+
+    dev = "cuda"
+
+    def bf16(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    fp8 = s.kv_dtype == "fp8_e4m3fn"
+    q = bf16(w.q)
+    k = torch.from_numpy(w.k_cache).to(dev) if fp8 else bf16(w.k_cache)
+    v = torch.from_numpy(w.v_cache).to(dev) if fp8 else bf16(w.v_cache)
+    i32 = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+    f32 = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+    seqlens = i32(w.seqlens) if s.layout != "ragged" else None
+    cu, bt, topk = i32(w.cu_seqlens), i32(w.block_table), i32(w.topk_idx)
+    ks, vs = f32(w.k_scale), f32(w.v_scale)
+    gate = bf16(w.gate) if w.gate is not None else None
+    if s.layout == "contiguous":
+        cap, kv_rows, mpp = w.k_cache.shape[1], w.k_cache.shape[0] * w.k_cache.shape[1], 0
+    elif s.layout == "ragged":
+        cap, kv_rows, mpp = 0, w.k_cache.shape[0], 0
+    else:
+        cap, kv_rows, mpp = 0, w.k_cache.shape[0] * s.page_size, w.block_table.shape[1]
+    params = G.make_params(batch=s.batch, s_q=s.s_q, h_q=s.h_q, h_kv=s.h_kv, head_dim=s.head_dim,
+                           layout=s.layout, kv_dtype=s.kv_dtype, causal=s.causal,
+                           max_seqlen_kv=w.max_seqlen, seq_capacity=cap, kv_rows=kv_rows,
+                           page_size=s.page_size, max_pages_per_seq=mpp, topk=s.topk,
+                           gate_mode="elementwise" if gate is not None else "none", kv_chunk=args.kv_chunk)
+    plan = G.gqa_decode_make_plan(params)
+    ws = torch.empty(max(plan["workspace_bytes"], 16), dtype=torch.uint8, device=dev)
+    o = torch.empty((s.batch, s.s_q, s.h_q, s.head_dim), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((s.batch, s.h_q, s.s_q), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    say(f"plan {plan}")
+
+    def step():
+        G.gqa_decode_run(params, q, k, v, seqlens, cu, bt, topk, ks, vs, gate, o, lse, ws, ws.numel(), stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Timed region: exactly K back-to-back calls; events around each partial
+    # kernel (recorded by the library on the launch stream) give its
+    # duration.
+    K = args.steps
+    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    for e in ev0 + ev1:
+        e.record(stream)            # creates the underlying hipEvent
+    torch.cuda.synchronize()
+    say(f"timing {K} steps")
+    t0 = time.perf_counter()
+    for i in range(K):
+        params.partial_event_begin = ev0[i].cuda_event
+        params.partial_event_end = ev1[i].cuda_event
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    params.partial_event_begin = None
+    params.partial_event_end = None
+    partial_ms = [ev0[i].elapsed_time(ev1[i]) for i in range(K)]
+    ms_per_step = wall * 1e3 / K
+    partial_us = statistics.mean(partial_ms) * 1e3
+    us_per_call = ms_per_step * 1e3
+    value = min_bytes / (us_per_call * 1e-6) / 1e9
+    achieved = kv_bytes / (partial_us * 1e-6) / 1e9
+    say(f"  {us_per_call:.2f} us/call, partial kernel {partial_us:.2f} us, {value:.1f} GB/s, "
+        f"partial {achieved:.1f} GB/s ({achieved / HBM_PEAK_GBPS:.1%} of 8 TB/s)")
+
+    extra = {}
+    if args.cold:
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        cold = []
+        for _ in range(20):
+            flush.zero_()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            step()
+            b.record(stream)
+            torch.cuda.synchronize()
+            cold.append(a.elapsed_time(b) * 1e3)
+        extra["us_per_call_cold_median"] = round(statistics.median(cold), 3)
+        del flush
+    if args.calibrate_copy:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(10):
+            dst.copy_(src)
+        b.record(stream)
+        torch.cuda.synchronize()
+        t_copy = a.elapsed_time(b) / 10 * 1e-3
+        extra["d2d_copy_512MiB_GBps"] = round(2 * (512 << 20) / t_copy / 1e9, 1)
+        del src, dst
+
+    traffic = read_traffic(args.workload)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3fn->bf16" if fp8 else "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": s.name, "batch": s.batch, "h_q": s.h_q, "h_kv": s.h_kv, "head_dim": s.head_dim,
+            "s_q": s.s_q, "kv_tokens": tokens, "layout": s.layout, "causal": s.causal, "topk": s.topk,
+            "kv_dtype": s.kv_dtype, "gate": w.gate is not None, "seed": w.seed,
+            "kv_chunk": plan["kv_chunk"], "num_splits": plan["num_splits"],
+        },
+        "us_per_call": round(us_per_call, 3),
+        "min_bytes_per_call": min_bytes,
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "gqa_partial_kernel",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": None if traffic is None else int(traffic),
+            "algorithmic_bytes_per_launch": kv_bytes,
+            "kernel_us": round(partial_us, 3),
+        },
+        **extra,
+    }
+    if not args.no_cpu_baseline:
+        say("timing the CPU oracle on a bounded sample")
+        line["cpu_baseline"] = cpu_baseline(w, min_bytes)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -21,7 +21,7 @@ hipError_t launch_partial(const DecodeArgs& a, int D, bool fp8, bool indirect, i
                           hipStream_t st);
 hipError_t launch_combine(const DecodeArgs& a, int D, dim3 grid, hipStream_t st);
 hipError_t launch_resolve(const DecodeArgs& a, int64_t* out, int list_cap, hipStream_t st);
-size_t partial_lds_bytes(int D, bool indirect, int chunk);
+size_t partial_lds_bytes(int D, bool fp8, bool indirect, int chunk);
 }  // namespace gqa
 
 namespace {
@@ -51,6 +51,10 @@ int log2_exact(int x) {
 }
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// KV heads per partial workgroup: four when H_kv allows (a workgroup then
+// reads 4 heads' contiguous slice of every token row), else two, else one.
+int heads_per_wg(int h_kv) { return h_kv % 4 == 0 ? 4 : (h_kv % 2 == 0 ? 2 : 1); }
 int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
 
 int device_cus() {
@@ -129,25 +133,25 @@ gqa_status make_plan(const gqa_decode_params* p, gqa_decode_plan* plan) {
   const bool indirect = p->layout == GQA_LAYOUT_PAGED || p->topk > 0;
   const int64_t L = p->topk > 0 ? p->topk : p->max_seqlen_kv;
   const int64_t pairs = (int64_t)p->batch * p->h_kv;
+  const int hpw = heads_per_wg(p->h_kv);
   int64_t chunk = p->kv_chunk;
   if (chunk == 0) {
     int cus = p->num_cus ? p->num_cus : device_cus();
     if (cus <= 0) return fail(GQA_ERR_HIP, "cannot query the device's compute-unit count");
-    // Aim for about four workgroups per CU in total (two resident per CU,
-    // two rounds), with at least 256 and at most 2048 list positions per
-    // workgroup, and never more than the list itself.
-    const int64_t target = 4LL * cus;
-    int64_t per = cdiv(std::max<int64_t>(pairs * L, 1), target);
+    // A workgroup covers hpw heads x chunk list positions.  Aim for about
+    // two workgroups per CU in total (one resident round), with between 256
+    // and 2048 positions per workgroup and never more than the list.
+    const int64_t target = 2LL * cus;
+    const int64_t per = cdiv(std::max<int64_t>(pairs * L, 1), target * hpw);
     chunk = round_up(std::max<int64_t>(per, 256), 128);
     chunk = std::min<int64_t>(chunk, 2048);
     chunk = std::min<int64_t>(chunk, round_up(std::max<int64_t>(L, 1), 32));
-    if (indirect) chunk = std::min<int64_t>(chunk, kMaxChunkIndirect);
   }
   const int64_t splits = std::max<int64_t>(1, cdiv(L, chunk));
   if (splits > INT32_MAX) return fail(GQA_ERR_UNSUPPORTED, "too many splits");
   plan->kv_chunk = (int32_t)chunk;
   plan->num_splits = (int32_t)splits;
-  plan->partial_workgroups = pairs * splits;
+  plan->partial_workgroups = (pairs / hpw) * splits;
   plan->combine = splits > 1 ? 1 : 0;
   if (splits > 1) {
     const size_t opart = (size_t)pairs * splits * rows * p->head_dim * sizeof(float);
@@ -180,6 +184,7 @@ void fill_args(gqa::DecodeArgs& a, const gqa_decode_params* p, const gqa_decode_
   a.gate_mode = p->gate_mode;
   a.chunk = plan.kv_chunk;
   a.num_splits = plan.num_splits;
+  a.heads_per_wg = heads_per_wg(p->h_kv);
   const float scale = p->softmax_scale != 0.f ? p->softmax_scale : 1.0f / std::sqrt((float)p->head_dim);
   a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
 }
@@ -276,7 +281,7 @@ gqa_status gqa_decode_run(const gqa_decode_params* p, const void* q, const void*
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool indirect = p->layout == GQA_LAYOUT_PAGED || p->topk > 0;
-  const dim3 grid(plan.num_splits, p->h_kv, p->batch);
+  const dim3 grid(plan.num_splits, p->h_kv / heads_per_wg(p->h_kv), p->batch);
   hipError_t e;
   if (p->partial_event_begin) {
     e = hipEventRecord(static_cast<hipEvent_t>(p->partial_event_begin), s);

@@ -12,6 +12,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kLayoutContiguous = 0;
 constexpr int kLayoutRagged = 1;
@@ -45,6 +46,7 @@ struct DecodeArgs {
   int32_t layout, causal, max_seqlen, seq_cap;
   int32_t page_shift, max_pages, topk_len, gate_mode;
   int32_t chunk, num_splits;
+  int32_t heads_per_wg;       // KV heads one partial workgroup covers (1, 2 or 4)
   float scale_log2;           // softmax scale * log2(e)
 };
 
@@ -76,6 +78,13 @@ __device__ __forceinline__ int slot_token(const DecodeArgs& a, int b, int n, int
   return (t >= 0 && t < n) ? t : -1;
 }
 
+// Contiguous / ragged layouts: the same row as token_row, without the
+// paged branch (a dependent load there would make the compiler drain all
+// outstanding memory operations at every join).
+__device__ __forceinline__ int64_t dense_row(const DecodeArgs& a, int t, int64_t base) {
+  return min(max(base + t, (int64_t)0), a.kv_rows - 1);
+}
+
 // Physical token row of logical token t (0 <= t < n) of request b, clamped
 // into the cache so that no offset can address memory outside it.
 __device__ __forceinline__ int64_t token_row(const DecodeArgs& a, int b, int t, int64_t base) {
@@ -83,10 +92,9 @@ __device__ __forceinline__ int64_t token_row(const DecodeArgs& a, int b, int t, 
   if (a.layout == kLayoutPaged) {
     const int page = a.block_table[(int64_t)b * a.max_pages + (t >> a.page_shift)];
     row = ((int64_t)page << a.page_shift) + (t & ((1 << a.page_shift) - 1));
-  } else {
-    row = base + t;
+    return min(max(row, (int64_t)0), a.kv_rows - 1);
   }
-  return min(max(row, (int64_t)0), a.kv_rows - 1);
+  return dense_row(a, t, base);
 }
 
 // ---------------------------------------------------------------------------
@@ -129,6 +137,15 @@ __device__ __forceinline__ void fp8x4_to_bf16x4(uint32_t w, uint32_t& lo, uint32
 __device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16).  Within each group of
+// 16 lanes, lane r's address names a row M[r] of four consecutive bf16; lane
+// i receives M[4k + i/4][i%4] for k = 0..3 (packed two per dword).
+__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
+  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+  bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(const_cast<uint16_t*>(p)));
+  return __builtin_bit_cast(uint2, v);
 }
 
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }

@@ -1,75 +1,116 @@
 // GQA decode kernels for gfx950 (MI355X).
 //
-// Split-KV partial kernel: one workgroup per (list chunk, KV head, request).
-// Its 4 waves walk the chunk in 32-position tiles (wave w takes tiles w,
-// w+4, ...).  Each K/V tile of the KV head is loaded from HBM once, with
-// 16-byte loads, and serves every query row of the group: the G query heads
-// times S_q query tokens, padded to 16-row MFMA blocks.  This is the
-// load-sharing the grouped kernels of "Sparse paged GQA decode attention
-// with FP8 KV cache on SM89" leave open ("Open problem"); the kernel never
-// expands K/V to H_q heads ("When the K/V copy costs more than the
-// attention").
+// Split-KV partial kernel.  A workgroup of 4 wave64s covers one list chunk
+// of one request for HPW consecutive KV heads (HPW = 4 when H_kv allows,
+// else 2 or 1).  Wave w works on head g0 + w % HPW; the 4 / HPW waves that
+// share a head take alternate 32-position tiles of the chunk and are merged
+// in LDS at the end.  With HPW = 4 the workgroup reads, for every token, a
+// contiguous 1 KiB of the cache (four heads' K or V), which is what lets
+// HBM run close to its streaming rate.
 //
-//   S^T (tokens x rows) = K (tokens x d) . Q^T (d x rows)     MFMA, K from registers
+// Each K/V tile of a head is loaded from HBM once and serves every query row
+// of the head's group: G = H_q / H_kv query heads times S_q query tokens,
+// padded to 16-row MFMA blocks.  This is the load sharing the grouped
+// kernels of "Sparse paged GQA decode attention with FP8 KV cache on SM89"
+// leave open ("Open problem"); K/V are never expanded to H_q heads ("When
+// the K/V copy costs more than the attention").
+//
+//   S^T (tokens x rows) = K (tokens x d) . Q^T (d x rows)         MFMA
 //   online softmax in base 2, scale folded into one multiplier
-//   O^T (d x rows)     += V^T (d x tokens) . P^T (tokens x rows)  MFMA, V^T from LDS
+//   O^T (d x rows)     += V^T (d x tokens) . P^T (tokens x rows)  MFMA
 //
-// K is loaded straight into the MFMA A-operand layout (lane = token, 8
-// consecutive d).  The contraction index of the QK product may be permuted
-// freely as long as Q uses the same permutation, which lets each lane issue
-// full 16-byte loads for both bf16 and FP8.  V must be contracted over
-// tokens, so each wave stages its V tile in LDS (XOR-swizzled rows) and
-// reads it back transposed.  The QK result already sits in the layout the PV
-// B operand needs (lane = query row, 4+4 tokens), so P never leaves
+// Loads are whole cache rows: one wave-wide 16-byte load covers 4 tokens x
+// 256 B (bf16, d=128), non-temporal since K/V are read once.  Both tiles
+// pass through per-wave LDS: K is re-read in the MFMA A-operand layout
+// (lane = token, 8 consecutive contraction slots; the contraction order
+// over d is free as long as Q uses the same one), V is read transposed
+// with ds_read_b64_tr_b16.  The QK result already sits in the layout the PV
+// B operand needs (lane = query row, 4 + 4 tokens), so P never leaves
 // registers.
 //
-// FP8 E4M3FN K/V are unpacked tile by tile in registers (never a dequantised
-// copy in memory, cf. "Profiling down to the register ...", Phase 4);
-// k_scale is folded into the score multiplier and v_scale applied once to
-// the output ("Sparse paged GQA decode attention ...", Implementations).
+// FP8 E4M3FN K/V are unpacked tile by tile (never a dequantised copy in
+// memory, cf. "Profiling down to the register, then an extension ...",
+// Phase 4); k_scale is folded into the score multiplier and v_scale is
+// applied once to the output ("Sparse paged GQA decode attention ...",
+// Implementations).
 //
-// The waves of a workgroup merge their (max, sum, acc) in LDS.  With one
-// split the workgroup writes the final bf16 O (times sigmoid(gate)) and the
-// natural-log LSE; otherwise it writes an fp32 partial (o_s, log2-sum-exp)
-// and the combine kernel merges the splits.
+// With one split the workgroup writes the final bf16 O (times
+// sigmoid(gate)) and the natural-log LSE; otherwise each head writes an
+// fp32 partial (o_s, log2-sum-exp) and the combine kernel merges the splits.
 
 #include <math.h>
 #include "gqa_device.h"
 
 namespace gqa {
 
-// Shared-memory footprint of the partial kernel.
-__host__ __device__ constexpr int vstage_bytes(int D) { return kWaves * kTile * D * 2; }
-__host__ __device__ constexpr int merge_bytes(int D) { return kWaves * 16 * D * 4 + 2 * kWaves * 16 * 4; }
-
 template <int D, bool FP8>
 struct TileShape {
   static constexpr int ESZ = FP8 ? 1 : 2;
-  static constexpr int KK = D / 32;            // MFMA k-steps over d
-  static constexpr int NB = D / 16;            // 16-wide d blocks of O
-  static constexpr int LD = D * ESZ / 64;      // 16-byte loads per token per lane
+  static constexpr int RB = D * ESZ;          // bytes of one head in one token row
+  static constexpr int CPR = RB / 16;         // 16-byte chunks per row (16, 8 or 4)
+  static constexpr int TPI = 64 / CPR;        // tokens per wave-wide load (4, 8 or 16)
+  static constexpr int NLD = kTile / TPI;     // wave-wide loads per tile per tensor
+  static constexpr int KK = D / 32;           // MFMA k-steps over d
+  static constexpr int NB = D / 16;           // 16-wide d blocks of O
 };
 
-// Element d of the QK contraction that (k-step kk, lane group qd, element j)
-// stands for.  bf16: each 16-byte load is one k-step; FP8: one 16-byte load
-// (16 codes) feeds two consecutive k-steps.
+// Shared memory of the partial kernel: per wave a K tile (raw 16-byte
+// chunks) and a V tile (bf16), statically allocated; after the tile loop
+// the same space holds the waves' fp32 accumulators.  The dynamic part
+// holds the resolved row table of paged / top-K chunks.
+__host__ __device__ constexpr int ktile_chunks(int D, bool fp8) { return kTile * D * (fp8 ? 1 : 2) / 16; }
+__host__ __device__ constexpr int vtile_elems(int D) { return kTile * D; }
+__host__ __device__ constexpr int wave_tile_bytes(int D, bool fp8) { return ktile_chunks(D, fp8) * 16 + vtile_elems(D) * 2; }
+__host__ __device__ constexpr size_t table_bytes(bool indirect, int chunk) { return indirect ? (size_t)chunk * 8 : 0; }
+
+// Contraction slot -> d.  K-step kk, lane group qd covers d = qk_d(kk, qd)
+// .. +7.  bf16: one 16-byte chunk per k-step (chunk 4 kk + qd); FP8: one
+// 16-byte chunk (16 codes, chunk 4 (kk / 2) + qd) feeds two k-steps.
 template <bool FP8>
 __device__ __forceinline__ int qk_d(int kk, int qd) {
   return FP8 ? (64 * (kk >> 1) + 16 * qd + 8 * (kk & 1)) : (32 * kk + 8 * qd);
 }
 
+// Physical 16-byte chunk of logical chunk c in the K tile row of token tok:
+// XOR by a token-dependent value so that the 16 rows one A-operand read
+// touches fall on distinct LDS banks.
+template <int CPR>
+__device__ __forceinline__ int kchunk(int c, int tok) {
+  return c ^ ((tok >> (CPR == 16 ? 0 : (CPR == 8 ? 1 : 2))) & (CPR - 1));
+}
+
+// Physical 16-element block of logical block blk in the V tile row of token
+// tok: the XOR spreads the 16 rows one transposed read touches over all
+// bank groups (d=128: a row is 8 blocks, one bank sweep; d=64: two rows
+// share a sweep).
+template <int D>
+__device__ __forceinline__ int vblk(int blk, int tok) {
+  return D == 128 ? (blk ^ (tok & 7)) : (blk ^ ((tok >> 1) & 3));
+}
+
 template <int D, bool FP8, bool INDIRECT, int MB>
-__global__ void __launch_bounds__(kThreads) gqa_partial_kernel(DecodeArgs a) {
+__global__ void __launch_bounds__(kThreads, MB == 1 ? 2 : 1) gqa_partial_kernel(DecodeArgs a) {
   using TS = TileShape<D, FP8>;
-  constexpr int KK = TS::KK, NB = TS::NB, LD = TS::LD, ESZ = TS::ESZ;
-  constexpr int R = MB * 16;
+  constexpr int RB = TS::RB, CPR = TS::CPR, TPI = TS::TPI, NLD = TS::NLD, KK = TS::KK, NB = TS::NB;
+  static_assert(kWaves * 16 * D * 4 <= kWaves * wave_tile_bytes(D, FP8), "accumulators fit in the tiles");
+
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __shared__ __attribute__((aligned(16))) unsigned char tiles[kWaves * wave_tile_bytes(D, FP8)];
+  __shared__ float wstat[2 * kWaves * 16];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // Wave index as a scalar: tile-level control flow is then uniform, which
+  // keeps branches scalar and the compiler's memory-counter waits precise.
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int m16 = lane & 15;
   const int qd = lane >> 4;
-  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int hpw = a.heads_per_wg;
+  const int wph = kWaves / hpw;                 // waves per head
+  const int hs = wave % hpw;                    // head slot of this wave
+  const int sub = wave / hpw;                   // this wave's share of the head's tiles
+  const int split = blockIdx.x, b = blockIdx.z;
+  const int g0 = blockIdx.y * hpw;
+  const int g = g0 + hs;
 
   const int n = seq_len(a, b);
   const int L = list_len(a, n);
@@ -79,7 +120,7 @@ __global__ void __launch_bounds__(kThreads) gqa_partial_kernel(DecodeArgs a) {
   const int ntiles = end > start ? (end - start + kTile - 1) / kTile : 0;
   const int64_t base = row_base(a, b);
 
-  int32_t* trow = reinterpret_cast<int32_t*>(smem + vstage_bytes(D));
+  int32_t* trow = reinterpret_cast<int32_t*>(smem);
   int32_t* ttok = trow + a.chunk;
   if constexpr (INDIRECT) {
     // Resolve every slot of the chunk once: physical row and logical token
@@ -133,52 +174,89 @@ __global__ void __launch_bounds__(kThreads) gqa_partial_kernel(DecodeArgs a) {
     for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  uint16_t* vs = reinterpret_cast<uint16_t*>(smem) + wave * kTile * D;
-  const size_t head_off = (size_t)g * D * ESZ;
-  const size_t row_bytes = (size_t)a.h_kv * D * ESZ;
+  unsigned char* wtiles = tiles + wave * wave_tile_bytes(D, FP8);
+  u32x4* kt = reinterpret_cast<u32x4*>(wtiles);
+  uint16_t* vt = reinterpret_cast<uint16_t*>(wtiles + ktile_chunks(D, FP8) * 16);
+  const size_t head_off = (size_t)g * RB;
+  const size_t row_bytes = (size_t)a.h_kv * RB;
+  const int ltok = lane / CPR;                  // token of this lane within a wave-wide load
+  const int lch = lane % CPR;                   // 16-byte chunk of this lane
 
-  // Issue the 16-byte loads of one tile: lane (m16, qd) fetches, for tokens
-  // m16 and 16 + m16 of the tile, bytes [64 j + 16 qd, +16) of the KV head.
-  auto load_tile = [&](int tile, u32x4 (&kr)[2][LD], u32x4 (&vr)[2][LD]) {
-    const int tb = start + tile * kTile;
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      const int p = tb + hb * 16 + m16;
-      int64_t row;
-      if constexpr (INDIRECT) {
-        row = trow[p - start];
-      } else {
-        row = token_row(a, b, p < end ? p : 0, base);
-      }
-      const size_t off = (size_t)row * row_bytes + head_off + 16 * qd;
-      const uint8_t* kp = a.k + off;
-      const uint8_t* vp = a.v + off;
-#pragma unroll
-      for (int j = 0; j < LD; ++j) kr[hb][j] = *reinterpret_cast<const u32x4*>(kp + 64 * j);
-#pragma unroll
-      for (int j = 0; j < LD; ++j) vr[hb][j] = *reinterpret_cast<const u32x4*>(vp + 64 * j);
+  auto row_of = [&](int p) -> int64_t {
+    if constexpr (INDIRECT) {
+      return trow[p - start];
+    } else {
+      return dense_row(a, p < end ? p : 0, base);
     }
   };
 
-  auto compute_tile = [&](int tile, const u32x4 (&kr)[2][LD], const u32x4 (&vr)[2][LD]) {
+  // Issue one tile's loads: NLD wave-wide 16-byte loads each for K and V,
+  // load i covering tokens i*TPI .. +TPI-1 of the tile in whole rows.  A
+  // non-real tile (the prefetch slot after a wave's last tile) reads one
+  // 16-byte location with every lane: no branch, no HBM traffic to speak of.
+  auto load_tile = [&](int tile, u32x4 (&kr)[NLD], u32x4 (&vr)[NLD], bool real) {
+    const int tb = start + tile * kTile;
+    const int lane_on = real ? 1 : 0;
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int64_t row = row_of(real ? tb + i * TPI + ltok : start);
+      const size_t off = (size_t)row * row_bytes + head_off + (size_t)(16 * lch * lane_on);
+      kr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.k + off));
+      vr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.v + off));
+    }
+  };
+
+  // Stage a tile's K (raw chunks) and V (bf16) in this wave's LDS tiles.
+  auto stage_tile = [&](const u32x4 (&kr)[NLD], const u32x4 (&vr)[NLD]) {
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int tok = i * TPI + ltok;
+      kt[tok * CPR + kchunk<CPR>(lch, tok)] = kr[i];
+      uint16_t* vrow = vt + tok * D;
+      if constexpr (FP8) {
+        // 16 codes = d [16 lch, +16) = one 16-element block
+        uint32_t x0, x1, x2, x3, y0, y1, y2, y3;
+        fp8x4_to_bf16x4(vr[i][0], x0, x1);
+        fp8x4_to_bf16x4(vr[i][1], x2, x3);
+        fp8x4_to_bf16x4(vr[i][2], y0, y1);
+        fp8x4_to_bf16x4(vr[i][3], y2, y3);
+        uint16_t* dst = vrow + 16 * vblk<D>(lch, tok);
+        *reinterpret_cast<u32x4*>(dst) = u32x4{x0, x1, x2, x3};
+        *reinterpret_cast<u32x4*>(dst + 8) = u32x4{y0, y1, y2, y3};
+      } else {
+        // 8 elements = d [8 lch, +8) = half of block lch / 2
+        *reinterpret_cast<u32x4*>(vrow + 16 * vblk<D>(lch >> 1, tok) + 8 * (lch & 1)) = vr[i];
+      }
+    }
+    // The writes above must land before other lanes read them; a wave's LDS
+    // operations execute in order, so a compiler barrier suffices.
+    __builtin_amdgcn_wave_barrier();
+    __asm__ __volatile__("" ::: "memory");
+  };
+
+  // Compute one staged tile (from LDS only).
+  auto compute_tile = [&](int tile) {
     const int tb = start + tile * kTile;
 
-    // K operands (bf16), unpacking FP8 in registers.
+    // K operands: lane (m16, qd) reads token 16 hb + m16, contraction chunk
+    // of k-step kk; FP8 chunks are unpacked to bf16 in registers.
     u32x4 kop[2][KK];
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
+      const int tok = hb * 16 + m16;
 #pragma unroll
-      for (int j = 0; j < LD; ++j) {
+      for (int j = 0; j < (FP8 ? KK / 2 : KK); ++j) {
+        const u32x4 c = kt[tok * CPR + kchunk<CPR>(4 * j + qd, tok)];
         if constexpr (FP8) {
           uint32_t x0, x1, x2, x3, y0, y1, y2, y3;
-          fp8x4_to_bf16x4(kr[hb][j][0], x0, x1);
-          fp8x4_to_bf16x4(kr[hb][j][1], x2, x3);
-          fp8x4_to_bf16x4(kr[hb][j][2], y0, y1);
-          fp8x4_to_bf16x4(kr[hb][j][3], y2, y3);
+          fp8x4_to_bf16x4(c[0], x0, x1);
+          fp8x4_to_bf16x4(c[1], x2, x3);
+          fp8x4_to_bf16x4(c[2], y0, y1);
+          fp8x4_to_bf16x4(c[3], y2, y3);
           kop[hb][2 * j] = u32x4{x0, x1, x2, x3};
           kop[hb][2 * j + 1] = u32x4{y0, y1, y2, y3};
         } else {
-          kop[hb][j] = kr[hb][j];
+          kop[hb][j] = c;
         }
       }
     }
@@ -193,32 +271,6 @@ __global__ void __launch_bounds__(kThreads) gqa_partial_kernel(DecodeArgs a) {
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) c = mfma_16x16x32(kop[hb][kk], qop[mb][kk], c);
         s[hb][mb] = c * sc;
-      }
-    }
-
-    // Stage V (as bf16) in this wave's LDS tile: row = token, 16-element
-    // blocks XOR-swizzled by (token / 4) % 4 so the transposed reads below
-    // hit four different bank groups.
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      const int tok = hb * 16 + m16;
-      const int swz = ((tok >> 2) & 3) << 4;
-      uint16_t* vrow = vs + tok * D;
-#pragma unroll
-      for (int j = 0; j < LD; ++j) {
-        if constexpr (FP8) {
-          const int d0 = 64 * j + 16 * qd;
-          uint32_t x0, x1, x2, x3, y0, y1, y2, y3;
-          fp8x4_to_bf16x4(vr[hb][j][0], x0, x1);
-          fp8x4_to_bf16x4(vr[hb][j][1], x2, x3);
-          fp8x4_to_bf16x4(vr[hb][j][2], y0, y1);
-          fp8x4_to_bf16x4(vr[hb][j][3], y2, y3);
-          *reinterpret_cast<u32x4*>(vrow + (d0 ^ swz)) = u32x4{x0, x1, x2, x3};
-          *reinterpret_cast<u32x4*>(vrow + ((d0 + 8) ^ swz)) = u32x4{y0, y1, y2, y3};
-        } else {
-          const int d0 = 32 * j + 8 * qd;
-          *reinterpret_cast<u32x4*>(vrow + (d0 ^ swz)) = vr[hb][j];
-        }
       }
     }
 
@@ -281,51 +333,77 @@ __global__ void __launch_bounds__(kThreads) gqa_partial_kernel(DecodeArgs a) {
       for (int nb = 0; nb < NB; ++nb) acc[mb][nb] *= alpha;
     }
 
-    // LDS writes above must land before other lanes read them; a wave's LDS
-    // operations execute in order, so a compiler barrier suffices.
-    __builtin_amdgcn_wave_barrier();
-    __asm__ __volatile__("" ::: "memory");
-
-    // V^T operand: lane (m16, qd) takes column d = 16 nb + m16 for tokens
-    // 4 qd + j and 16 + 4 qd + j (j < 4), matching P's k-slot order.
+    // V^T operand: lane (m16, qd) needs column d = 16 nb + m16 for tokens
+    // 4 qd + k and 16 + 4 qd + k (k < 4), matching P's k-slot order.  One
+    // ds_read_b64_tr_b16 delivers four of them: within each 16-lane group,
+    // lane r supplies the address of 4 consecutive bf16 of row
+    // M[r] = V[tok(r)][16 nb + 4 (r & 3) .. +3], tok(r) = 4 qd + r / 4, and
+    // lane i receives M[4 k + i / 4][i % 4] = V[4 qd + k][16 nb + i].
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const int col = ((nb ^ qd) << 4) + m16;
       uint32_t w[4];
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const int t0 = 4 * qd + 2 * jj;
-        const uint32_t a0 = vs[(t0)*D + col];
-        const uint32_t a1 = vs[(t0 + 1) * D + col];
-        const uint32_t b0 = vs[(16 + t0) * D + col];
-        const uint32_t b1 = vs[(16 + t0 + 1) * D + col];
-        w[jj] = a0 | (a1 << 16);
-        w[2 + jj] = b0 | (b1 << 16);
+      for (int hf = 0; hf < 2; ++hf) {
+        const int tok = 16 * hf + 4 * qd + (m16 >> 2);
+        const uint2 t = lds_read_tr16(vt + tok * D + 16 * vblk<D>(nb, tok) + 4 * (m16 & 3));
+        w[2 * hf] = t.x;
+        w[2 * hf + 1] = t.y;
       }
       const u32x4 av = {w[0], w[1], w[2], w[3]};
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) acc[mb][nb] = mfma_16x16x32(av, pB[mb], acc[mb][nb]);
     }
+    // All reads of this tile's LDS are done before the next tile is staged.
     __builtin_amdgcn_wave_barrier();
     __asm__ __volatile__("" ::: "memory");
   };
 
-  // Software pipeline: the next tile's loads are in flight while this one
-  // is computed.
+  // Keeps every load issued so far above this point: no IR pass may sink a
+  // load past a possible memory write, and the machine scheduler may not
+  // move instructions across the barrier.
+  auto issue_fence = [] {
+    __asm__ __volatile__("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // Software pipeline over the wave's tiles (tile, tile + wph, ...), two
+  // register buffers: each step stages the current tile's registers into
+  // LDS, at once refills the same registers with the tile two steps ahead
+  // (a dummy past the end), then computes from LDS -- so two tiles of loads
+  // are in flight while a tile is computed.  Every step is one straight-line
+  // block, so the compiler cannot hoist work above the loads and its waits
+  // leave the younger tile in flight.
   {
-    u32x4 kA[2][LD], vA[2][LD], kB[2][LD], vB[2][LD];
-    int tile = wave;
-    if (tile < ntiles) load_tile(tile, kA, vA);
-    while (tile < ntiles) {
-      int nxt = tile + kWaves;
-      if (nxt < ntiles) load_tile(nxt, kB, vB);
-      compute_tile(tile, kA, vA);
-      tile = nxt;
-      if (tile >= ntiles) break;
-      nxt = tile + kWaves;
-      if (nxt < ntiles) load_tile(nxt, kA, vA);
-      compute_tile(tile, kB, vB);
-      tile = nxt;
+    u32x4 kA[NLD], vA[NLD], kB[NLD], vB[NLD];
+    int tile = sub;
+    if (tile < ntiles) {
+      load_tile(tile, kA, vA, true);
+      issue_fence();  // keep the first tile's loads older than the second's
+      const bool second = tile + wph < ntiles;
+      load_tile(second ? tile + wph : tile, kB, vB, second);
+      issue_fence();
+      while (true) {
+        stage_tile(kA, vA);
+        issue_fence();  // the staged registers are dead before they are refilled
+        int ahead = tile + 2 * wph;
+        bool real = ahead < ntiles;
+        load_tile(real ? ahead : tile, kA, vA, real);
+        issue_fence();
+        compute_tile(tile);
+        issue_fence();
+        tile += wph;
+        if (tile >= ntiles) break;
+        stage_tile(kB, vB);
+        issue_fence();  // the staged registers are dead before they are refilled
+        ahead = tile + 2 * wph;
+        real = ahead < ntiles;
+        load_tile(real ? ahead : tile, kB, vB, real);
+        issue_fence();
+        compute_tile(tile);
+        issue_fence();
+        tile += wph;
+        if (tile >= ntiles) break;
+      }
     }
   }
 
@@ -336,12 +414,12 @@ __global__ void __launch_bounds__(kThreads) gqa_partial_kernel(DecodeArgs a) {
     lrun[mb] += __shfl_xor(lrun[mb], 32);
   }
 
-  // Merge the four waves, one 16-row block at a time.
-  float* wm = reinterpret_cast<float*>(smem);
-  float* wl = wm + kWaves * 16;
-  float* wacc = wl + kWaves * 16;
-  const float vsc = FP8 ? a.v_scale[b * a.h_kv + g] : 1.f;
+  // Merge the waves of each head, one 16-row block at a time, and write.
+  float* wacc = reinterpret_cast<float*>(tiles);
+  float* wm = wstat;
+  float* wl = wstat + kWaves * 16;
   const bool final_out = (a.num_splits == 1);
+  constexpr int D8 = D / 8;
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     if (mb * 16 >= a.rows) break;
@@ -356,21 +434,23 @@ __global__ void __launch_bounds__(kThreads) gqa_partial_kernel(DecodeArgs a) {
     __syncthreads();
 
     const int nrow = min(16, a.rows - mb * 16);
-    for (int it = threadIdx.x; it < nrow * (D / 8); it += kThreads) {
-      const int rl = it / (D / 8);
-      const int d8 = it - rl * (D / 8);
+    for (int it = threadIdx.x; it < hpw * nrow * D8; it += kThreads) {
+      const int hh = it / (nrow * D8);
+      const int rem = it - hh * (nrow * D8);
+      const int rl = rem / D8;
+      const int d8 = rem - rl * D8;
       const int r = mb * 16 + rl;
+      const int gg = g0 + hh;
       float M = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, wm[w * 16 + rl]);
+      for (int k = 0; k < wph; ++k) M = fmaxf(M, wm[(hh + k * hpw) * 16 + rl]);
       float o[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[e] = 0.f;
       float lse2 = -INFINITY;
       if (M != -INFINITY) {
         float sum = 0.f;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
+        for (int k = 0; k < wph; ++k) {
+          const int w = hh + k * hpw;
           const float e = fast_exp2(wm[w * 16 + rl] - M);
           sum += e * wl[w * 16 + rl];
           const float* src = wacc + (w * 16 + rl) * D + d8 * 8;
@@ -382,13 +462,13 @@ __global__ void __launch_bounds__(kThreads) gqa_partial_kernel(DecodeArgs a) {
             o[4 + c] += e * x1[c];
           }
         }
-        const float inv = vsc / sum;
+        const float inv = (FP8 ? a.v_scale[b * a.h_kv + gg] : 1.f) / sum;
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[e] *= inv;
         lse2 = M + __log2f(sum);
       }
       const int i = r / a.group;
-      const int h = g * a.group + (r - i * a.group);
+      const int h = gg * a.group + (r - i * a.group);
       if (final_out) {
         const int64_t oidx = ((int64_t)(b * a.s_q + i) * a.h_q + h) * D + d8 * 8;
         if (a.gate_mode == kGateElementwise) {
@@ -409,7 +489,7 @@ __global__ void __launch_bounds__(kThreads) gqa_partial_kernel(DecodeArgs a) {
         *reinterpret_cast<u32x4*>(a.o + oidx) = ov;
         if (d8 == 0) a.lse[((int64_t)b * a.h_q + h) * a.s_q + i] = lse2 * 0.69314718055994530942f;
       } else {
-        const int64_t prow = ((int64_t)(b * a.h_kv + g) * a.num_splits + split) * a.rows + r;
+        const int64_t prow = ((int64_t)(b * a.h_kv + gg) * a.num_splits + split) * a.rows + r;
         float* dst = a.o_part + prow * D + d8 * 8;
         *reinterpret_cast<f32x4*>(dst) = f32x4{o[0], o[1], o[2], o[3]};
         *reinterpret_cast<f32x4*>(dst + 4) = f32x4{o[4], o[5], o[6], o[7]};
@@ -422,67 +502,98 @@ __global__ void __launch_bounds__(kThreads) gqa_partial_kernel(DecodeArgs a) {
 // LSE combine: one workgroup per (query row of the group, KV head, request).
 // With M = max_s lse_s (base 2), O = sum_s 2^(lse_s - M) o_s / sum_s 2^(lse_s - M)
 // and LSE = ln 2 * (M + log2 sum_s 2^(lse_s - M)); empty splits (-inf) weigh 0.
+// Thread (column quad d4, split lane sg) owns splits sg, sg + SG, ...; it
+// issues all their loads at once and merges them with a private running
+// maximum, and the split lanes are merged once through LDS.
 template <int D>
 __global__ void __launch_bounds__(kThreads) gqa_combine_kernel(DecodeArgs a) {
   constexpr int Q4 = D / 4;          // float4 columns
   constexpr int SG = kThreads / Q4;  // split lanes
-  __shared__ f32x4 red[SG][Q4];
+  constexpr int UNROLL = 8;          // splits per thread per round
+  __shared__ f32x4 racc[SG][Q4];
+  __shared__ float rm[SG], rl[SG];
   const int r = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x & 63;
   const int n = seq_len(a, b);
   const int L = list_len(a, n);
   const int nsp = min(a.num_splits, (L + a.chunk - 1) / a.chunk);
   const int64_t first = (int64_t)(b * a.h_kv + g) * a.num_splits;
   const float* lsep = a.lse_part + first * a.rows + r;
   const float* op = a.o_part + (first * a.rows + r) * D;
-
-  float M = -INFINITY;
-  for (int s = lane; s < nsp; s += 64) M = fmaxf(M, lsep[(int64_t)s * a.rows]);
-  M = wave_max(M);
-  float S = 0.f;
-  if (M != -INFINITY)
-    for (int s = lane; s < nsp; s += 64) S += fast_exp2(lsep[(int64_t)s * a.rows] - M);
-  S = wave_sum(S);
-
   const int d4 = threadIdx.x % Q4;
   const int sg = threadIdx.x / Q4;
+
+  float m = -INFINITY, l = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  if (M != -INFINITY) {
-    for (int s = sg; s < nsp; s += SG) {
-      const float w = fast_exp2(lsep[(int64_t)s * a.rows] - M);
-      const f32x4 x = *reinterpret_cast<const f32x4*>(op + (int64_t)s * a.rows * D + d4 * 4);
-      acc += w * x;
+  for (int s0 = sg; s0 < nsp; s0 += SG * UNROLL) {
+    float ls[UNROLL];
+    f32x4 x[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int sidx = min(s0 + u * SG, nsp - 1);
+      ls[u] = lsep[(int64_t)sidx * a.rows];
+      x[u] = *reinterpret_cast<const f32x4*>(op + (int64_t)sidx * a.rows * D + d4 * 4);
+    }
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u)
+      if (s0 + u * SG >= nsp) ls[u] = -INFINITY;
+    float mx = m;
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) mx = fmaxf(mx, ls[u]);
+    if (mx != -INFINITY) {
+      const float alpha = fast_exp2(m - mx);
+      acc *= alpha;
+      l *= alpha;
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+        const float w = fast_exp2(ls[u] - mx);
+        l += w;
+        acc += w * x[u];
+      }
+      m = mx;
     }
   }
-  red[sg][d4] = acc;
+  racc[sg][d4] = acc;
+  if (d4 == 0) {
+    rm[sg] = m;
+    rl[sg] = l;
+  }
   __syncthreads();
-  if (sg == 0) {
-    for (int k = 1; k < SG; ++k) acc += red[k][d4];
-    float o[4] = {0.f, 0.f, 0.f, 0.f};
-    if (M != -INFINITY) {
-      const float inv = 1.f / S;
+  if (sg != 0) return;
+  float M = -INFINITY;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) o[c] = acc[c] * inv;
-    }
-    const int i = r / a.group;
-    const int h = g * a.group + (r - i * a.group);
-    const int64_t oidx = ((int64_t)(b * a.s_q + i) * a.h_q + h) * D + d4 * 4;
-    if (a.gate_mode == kGateElementwise) {
-      const uint2 gw = *reinterpret_cast<const uint2*>(a.gate + oidx);
-      o[0] *= sigmoidf_(bf16_lo(gw.x));
-      o[1] *= sigmoidf_(bf16_hi(gw.x));
-      o[2] *= sigmoidf_(bf16_lo(gw.y));
-      o[3] *= sigmoidf_(bf16_hi(gw.y));
-    } else if (a.gate_mode == kGateHeadwise) {
-      const float sgm = sigmoidf_(bf16_lo(a.gate[(int64_t)(b * a.s_q + i) * a.h_q + h]));
+  for (int k = 0; k < SG; ++k) M = fmaxf(M, rm[k]);
+  float o[4] = {0.f, 0.f, 0.f, 0.f};
+  float lse2 = -INFINITY;
+  if (M != -INFINITY) {
+    float S = 0.f;
+    f32x4 t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < 4; ++c) o[c] *= sgm;
+    for (int k = 0; k < SG; ++k) {
+      const float w = fast_exp2(rm[k] - M);
+      S += w * rl[k];
+      t += w * racc[k][d4];
     }
-    *reinterpret_cast<uint2*>(a.o + oidx) = uint2{pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3])};
-    if (d4 == 0)
-      a.lse[((int64_t)b * a.h_q + h) * a.s_q + i] =
-          (M == -INFINITY) ? -INFINITY : (M + __log2f(S)) * 0.69314718055994530942f;
+    const float inv = 1.f / S;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) o[c] = t[c] * inv;
+    lse2 = M + __log2f(S);
   }
+  const int i = r / a.group;
+  const int h = g * a.group + (r - i * a.group);
+  const int64_t oidx = ((int64_t)(b * a.s_q + i) * a.h_q + h) * D + d4 * 4;
+  if (a.gate_mode == kGateElementwise) {
+    const uint2 gw = *reinterpret_cast<const uint2*>(a.gate + oidx);
+    o[0] *= sigmoidf_(bf16_lo(gw.x));
+    o[1] *= sigmoidf_(bf16_hi(gw.x));
+    o[2] *= sigmoidf_(bf16_lo(gw.y));
+    o[3] *= sigmoidf_(bf16_hi(gw.y));
+  } else if (a.gate_mode == kGateHeadwise) {
+    const float sgm = sigmoidf_(bf16_lo(a.gate[(int64_t)(b * a.s_q + i) * a.h_q + h]));
+#pragma unroll
+    for (int c = 0; c < 4; ++c) o[c] *= sgm;
+  }
+  *reinterpret_cast<uint2*>(a.o + oidx) = uint2{pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3])};
+  if (d4 == 0) a.lse[((int64_t)b * a.h_q + h) * a.s_q + i] = lse2 * 0.69314718055994530942f;
 }
 
 // Address resolution only, through the same slot_token / token_row the
@@ -507,8 +618,7 @@ __global__ void __launch_bounds__(kThreads) gqa_resolve_kernel(DecodeArgs a, int
 
 template <int D, bool FP8, bool IND, int MB>
 static hipError_t launch_partial_t(const DecodeArgs& a, dim3 grid, hipStream_t st) {
-  size_t lds = (size_t)vstage_bytes(D) + (IND ? (size_t)a.chunk * 8 : 0);
-  lds = lds > (size_t)merge_bytes(D) ? lds : (size_t)merge_bytes(D);
+  const size_t lds = table_bytes(IND, a.chunk);
   hipLaunchKernelGGL((gqa_partial_kernel<D, FP8, IND, MB>), grid, dim3(kThreads), lds, st, a);
   return hipGetLastError();
 }
@@ -522,9 +632,8 @@ static hipError_t launch_mb(const DecodeArgs& a, int mb, dim3 grid, hipStream_t 
   }
 }
 
-size_t partial_lds_bytes(int D, bool indirect, int chunk) {
-  size_t lds = (size_t)vstage_bytes(D) + (indirect ? (size_t)chunk * 8 : 0);
-  return lds > (size_t)merge_bytes(D) ? lds : (size_t)merge_bytes(D);
+size_t partial_lds_bytes(int D, bool fp8, bool indirect, int chunk) {
+  return (size_t)kWaves * wave_tile_bytes(D, fp8) + 2 * kWaves * 16 * 4 + table_bytes(indirect, chunk);
 }
 
 hipError_t launch_partial(const DecodeArgs& a, int D, bool fp8, bool indirect, int mb, dim3 grid,
