@@ -27,6 +27,8 @@ import statistics
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -90,27 +92,54 @@ def workload_bytes(w):
 def cpu_baseline(w, min_bytes, budget_s=10.0):
     """The fp64 oracle on whole KV heads of the same workload (one BLAS
     thread), KV head by KV head until ``budget_s`` is used; throughput is
-    scaled to the sampled share of the minimum bytes."""
+    scaled to the sampled share of the minimum bytes.  Also returns the
+    oracle's outputs for the sampled rows."""
     import oracle.reference as R
     from threadpoolctl import threadpool_limits
     s = w.spec
     G = s.h_q // s.h_kv
     t0 = time.perf_counter()
     heads = 0
+    rows = []
+    O = L = None
     with threadpool_limits(1):
         for g in range(s.h_kv):
-            rows = [(b, i, h) for b in range(s.batch) for i in range(s.s_q) for h in range(g * G, (g + 1) * G)]
-            R.reference_decode(**w.arrays(), **w.params(), rows=rows)
+            rg = [(b, i, h) for b in range(s.batch) for i in range(s.s_q) for h in range(g * G, (g + 1) * G)]
+            Og, Lg = R.reference_decode(**w.arrays(), **w.params(), rows=rg,
+                                        gate_mode="elementwise")
+            if O is None:
+                O, L = Og, Lg
+            else:
+                sel = ~np.isnan(Og[..., 0])
+                O[sel] = Og[sel]
+                L[~np.isnan(Lg)] = Lg[~np.isnan(Lg)]
+            rows += rg
             heads += 1
             if time.perf_counter() - t0 >= budget_s:
                 break
     dt = time.perf_counter() - t0
     frac = heads / s.h_kv
-    return {"value": round(min_bytes * frac / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{heads} of {s.h_kv} KV heads ({heads * G * s.s_q * s.batch} of "
-                      f"{s.h_q * s.s_q * s.batch} query rows), {dt:.1f} s on "
-                      f"{platform.processor() or platform.machine()}",
-            "seconds": round(dt, 2)}
+    res = {"value": round(min_bytes * frac / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+           "sample": f"{heads} of {s.h_kv} KV heads ({len(rows)} of {s.h_q * s.s_q * s.batch} query rows), "
+                     f"{dt:.1f} s on {platform.processor() or platform.machine()}",
+           "seconds": round(dt, 2)}
+    return res, rows, O, L
+
+
+def check_against_oracle(o_gpu, lse_gpu, rows, Oref, Lref, fp8):
+    """Max errors of the GPU outputs on the oracle's sampled rows."""
+    b = np.array([r[0] for r in rows])
+    i = np.array([r[1] for r in rows])
+    h = np.array([r[2] for r in rows])
+    O = o_gpu.float().cpu().numpy()[b, i, h].astype(np.float64)
+    L = lse_gpu.cpu().numpy()[b, h, i].astype(np.float64)
+    Or, Lr = Oref[b, i, h], Lref[b, h, i]
+    fin = np.isfinite(Lr)
+    o_err = float(np.abs(O - Or).max())
+    l_err = float(np.abs(L[fin] - Lr[fin]).max()) if fin.any() else 0.0
+    ok = (o_err <= (6e-2 if fp8 else 2e-2) and l_err <= 1e-3 and
+          np.array_equal(np.isneginf(L), np.isneginf(Lr)))
+    return {"rows": len(rows), "o_max_abs_err": o_err, "lse_max_abs_err": l_err, "ok": bool(ok)}
 
 
 def main():
@@ -133,7 +162,6 @@ def main():
               "the decode path has no multi-GPU mode in this build", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import gqa_inputs as gi
@@ -285,10 +313,17 @@ def main():
         },
         **extra,
     }
+    ok = True
     if not args.no_cpu_baseline:
         say("timing the CPU oracle on a bounded sample")
-        line["cpu_baseline"] = cpu_baseline(w, min_bytes)
+        res, rows, Oref, Lref = cpu_baseline(w, min_bytes)
+        line["cpu_baseline"] = res
+        line["check"] = check_against_oracle(o, lse, rows, Oref, Lref, fp8)
+        ok = line["check"]["ok"]
     print(json.dumps(line), flush=True)
+    if not ok:
+        say("GPU output does not match the oracle on the sampled rows")
+        sys.exit(1)
 
 
 if __name__ == "__main__":

@@ -18,7 +18,7 @@
 
 namespace gqa {
 hipError_t launch_partial(const DecodeArgs& a, int D, bool fp8, bool indirect, int mb, dim3 grid,
-                          hipStream_t st);
+                          hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_combine(const DecodeArgs& a, int D, dim3 grid, hipStream_t st);
 hipError_t launch_resolve(const DecodeArgs& a, int64_t* out, int list_cap, hipStream_t st);
 size_t partial_lds_bytes(int D, bool fp8, bool indirect, int chunk);
@@ -40,6 +40,7 @@ gqa_status fail(gqa_status s, const char* fmt, ...) {
 }
 
 constexpr int kMaxChunkIndirect = 4096;
+constexpr size_t kMaxLdsPerWorkgroup = 160 * 1024;  // gfx950: 160 KiB of LDS per CU and workgroup
 constexpr int kMaxRows = 64;
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -55,6 +56,7 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // KV heads per partial workgroup: four when H_kv allows (a workgroup then
 // reads 4 heads' contiguous slice of every token row), else two, else one.
 int heads_per_wg(int h_kv) { return h_kv % 4 == 0 ? 4 : (h_kv % 2 == 0 ? 2 : 1); }
+static_assert(gqa::kPWaves % 4 == 0, "heads per workgroup must divide the waves");
 int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
 
 int device_cus() {
@@ -139,14 +141,24 @@ gqa_status make_plan(const gqa_decode_params* p, gqa_decode_plan* plan) {
     int cus = p->num_cus ? p->num_cus : device_cus();
     if (cus <= 0) return fail(GQA_ERR_HIP, "cannot query the device's compute-unit count");
     // A workgroup covers hpw heads x chunk list positions.  Aim for about
-    // two workgroups per CU in total (one resident round), with between 256
-    // and 2048 positions per workgroup and never more than the list.
-    const int64_t target = 2LL * cus;
-    const int64_t per = cdiv(std::max<int64_t>(pairs * L, 1), target * hpw);
-    chunk = round_up(std::max<int64_t>(per, 256), 128);
-    chunk = std::min<int64_t>(chunk, 2048);
+    // one workgroup per CU over the whole grid (MI355X measurements: one
+    // resident round of long workgroups streams best and writes the fewest
+    // partials), with 128..2048 positions per workgroup and never more than
+    // the list.  A ragged batch whose lengths vary (its packed cache holds
+    // fewer than batch * max_seqlen_kv rows) takes at most 1024 so that
+    // requests of very different lengths still balance across CUs.
+    const int64_t per = cdiv(std::max<int64_t>(pairs * L, 1), (int64_t)cus * hpw);
+    const bool varied = p->layout == GQA_LAYOUT_RAGGED && p->kv_rows < (int64_t)p->batch * p->max_seqlen_kv;
+    chunk = round_up(std::max<int64_t>(per, 128), 128);
+    chunk = std::min<int64_t>(chunk, varied ? 1024 : 4096);
     chunk = std::min<int64_t>(chunk, round_up(std::max<int64_t>(L, 1), 32));
   }
+  // Shared memory of one partial workgroup (per-wave K/V tiles plus the
+  // row table of paged / top-K chunks) must fit a workgroup's LDS.
+  const size_t lds = gqa::partial_lds_bytes(p->head_dim, p->kv_dtype == GQA_KV_FP8_E4M3FN, indirect, (int)chunk);
+  if (lds > kMaxLdsPerWorkgroup)
+    return fail(GQA_ERR_UNSUPPORTED, "kv_chunk %lld needs %zu bytes of LDS per workgroup (limit %zu)",
+                (long long)chunk, lds, kMaxLdsPerWorkgroup);
   const int64_t splits = std::max<int64_t>(1, cdiv(L, chunk));
   if (splits > INT32_MAX) return fail(GQA_ERR_UNSUPPORTED, "too many splits");
   plan->kv_chunk = (int32_t)chunk;
@@ -282,17 +294,10 @@ gqa_status gqa_decode_run(const gqa_decode_params* p, const void* q, const void*
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool indirect = p->layout == GQA_LAYOUT_PAGED || p->topk > 0;
   const dim3 grid(plan.num_splits, p->h_kv / heads_per_wg(p->h_kv), p->batch);
-  hipError_t e;
-  if (p->partial_event_begin) {
-    e = hipEventRecord(static_cast<hipEvent_t>(p->partial_event_begin), s);
-    if (e != hipSuccess) return hip_fail(e, "hipEventRecord(begin)");
-  }
-  e = gqa::launch_partial(a, p->head_dim, p->kv_dtype == GQA_KV_FP8_E4M3FN, indirect, plan.row_blocks, grid, s);
+  hipError_t e = gqa::launch_partial(a, p->head_dim, p->kv_dtype == GQA_KV_FP8_E4M3FN, indirect, plan.row_blocks,
+                                     grid, s, static_cast<hipEvent_t>(p->partial_event_begin),
+                                     static_cast<hipEvent_t>(p->partial_event_end));
   if (e != hipSuccess) return hip_fail(e, "partial kernel launch");
-  if (p->partial_event_end) {
-    e = hipEventRecord(static_cast<hipEvent_t>(p->partial_event_end), s);
-    if (e != hipSuccess) return hip_fail(e, "hipEventRecord(end)");
-  }
   if (plan.combine) {
     e = gqa::launch_combine(a, p->head_dim, dim3(plan.rows, p->h_kv, p->batch), s);
     if (e != hipSuccess) return hip_fail(e, "combine kernel launch");

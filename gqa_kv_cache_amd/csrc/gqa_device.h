@@ -21,9 +21,16 @@ constexpr int kGateNone = 0;
 constexpr int kGateElementwise = 1;
 constexpr int kGateHeadwise = 2;
 
-constexpr int kThreads = 256;   // 4 wave64s per workgroup
+constexpr int kThreads = 256;   // 4 wave64s per workgroup (combine, resolve)
 constexpr int kWaves = 4;
 constexpr int kTile = 32;       // list positions per wave iteration
+
+// Waves per split-KV partial workgroup (a build-time tuning constant).
+#ifndef GQA_PARTIAL_WAVES
+#define GQA_PARTIAL_WAVES 4
+#endif
+constexpr int kPWaves = GQA_PARTIAL_WAVES;
+constexpr int kPThreads = 64 * kPWaves;
 
 // Everything a kernel needs, passed by value (kernarg segment).
 struct DecodeArgs {

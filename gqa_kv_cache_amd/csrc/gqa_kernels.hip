@@ -38,6 +38,7 @@
 // sigmoid(gate)) and the natural-log LSE; otherwise each head writes an
 // fp32 partial (o_s, log2-sum-exp) and the combine kernel merges the splits.
 
+#include <hip/hip_ext.h>
 #include <math.h>
 #include "gqa_device.h"
 
@@ -89,14 +90,14 @@ __device__ __forceinline__ int vblk(int blk, int tok) {
 }
 
 template <int D, bool FP8, bool INDIRECT, int MB>
-__global__ void __launch_bounds__(kThreads, MB == 1 ? 2 : 1) gqa_partial_kernel(DecodeArgs a) {
+__global__ void __launch_bounds__(kPThreads, MB == 1 ? 2 : 1) gqa_partial_kernel(DecodeArgs a) {
   using TS = TileShape<D, FP8>;
   constexpr int RB = TS::RB, CPR = TS::CPR, TPI = TS::TPI, NLD = TS::NLD, KK = TS::KK, NB = TS::NB;
-  static_assert(kWaves * 16 * D * 4 <= kWaves * wave_tile_bytes(D, FP8), "accumulators fit in the tiles");
+  static_assert(kPWaves * 16 * D * 4 <= kPWaves * wave_tile_bytes(D, FP8), "accumulators fit in the tiles");
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  __shared__ __attribute__((aligned(16))) unsigned char tiles[kWaves * wave_tile_bytes(D, FP8)];
-  __shared__ float wstat[2 * kWaves * 16];
+  __shared__ __attribute__((aligned(16))) unsigned char tiles[kPWaves * wave_tile_bytes(D, FP8)];
+  __shared__ float wstat[2 * kPWaves * 16];
 
   const int lane = threadIdx.x & 63;
   // Wave index as a scalar: tile-level control flow is then uniform, which
@@ -105,7 +106,7 @@ __global__ void __launch_bounds__(kThreads, MB == 1 ? 2 : 1) gqa_partial_kernel(
   const int m16 = lane & 15;
   const int qd = lane >> 4;
   const int hpw = a.heads_per_wg;
-  const int wph = kWaves / hpw;                 // waves per head
+  const int wph = kPWaves / hpw;                 // waves per head
   const int hs = wave % hpw;                    // head slot of this wave
   const int sub = wave / hpw;                   // this wave's share of the head's tiles
   const int split = blockIdx.x, b = blockIdx.z;
@@ -125,7 +126,7 @@ __global__ void __launch_bounds__(kThreads, MB == 1 ? 2 : 1) gqa_partial_kernel(
   if constexpr (INDIRECT) {
     // Resolve every slot of the chunk once: physical row and logical token
     // (-1 = masked).  Slots past the end are masked.
-    for (int p = threadIdx.x; p < a.chunk; p += kThreads) {
+    for (int p = threadIdx.x; p < a.chunk; p += kPThreads) {
       const int pos = start + p;
       int t = -1;
       int64_t row = 0;
@@ -417,7 +418,7 @@ __global__ void __launch_bounds__(kThreads, MB == 1 ? 2 : 1) gqa_partial_kernel(
   // Merge the waves of each head, one 16-row block at a time, and write.
   float* wacc = reinterpret_cast<float*>(tiles);
   float* wm = wstat;
-  float* wl = wstat + kWaves * 16;
+  float* wl = wstat + kPWaves * 16;
   const bool final_out = (a.num_splits == 1);
   constexpr int D8 = D / 8;
 #pragma unroll
@@ -434,7 +435,7 @@ __global__ void __launch_bounds__(kThreads, MB == 1 ? 2 : 1) gqa_partial_kernel(
     __syncthreads();
 
     const int nrow = min(16, a.rows - mb * 16);
-    for (int it = threadIdx.x; it < hpw * nrow * D8; it += kThreads) {
+    for (int it = threadIdx.x; it < hpw * nrow * D8; it += kPThreads) {
       const int hh = it / (nrow * D8);
       const int rem = it - hh * (nrow * D8);
       const int rl = rem / D8;
@@ -616,34 +617,44 @@ __global__ void __launch_bounds__(kThreads) gqa_resolve_kernel(DecodeArgs a, int
 // Host-side launchers (called from the C ABI in gqa_api.cpp).
 // ---------------------------------------------------------------------------
 
+// ev0 / ev1 (may be null): events stamped by the dispatch itself at the
+// kernel's start and end, so they time the kernel alone.
 template <int D, bool FP8, bool IND, int MB>
-static hipError_t launch_partial_t(const DecodeArgs& a, dim3 grid, hipStream_t st) {
+static hipError_t launch_partial_t(const DecodeArgs& a, dim3 grid, hipStream_t st, hipEvent_t ev0,
+                                   hipEvent_t ev1) {
   const size_t lds = table_bytes(IND, a.chunk);
-  hipLaunchKernelGGL((gqa_partial_kernel<D, FP8, IND, MB>), grid, dim3(kThreads), lds, st, a);
+  hipExtLaunchKernelGGL((gqa_partial_kernel<D, FP8, IND, MB>), grid, dim3(kPThreads), lds, st, ev0, ev1, 0, a);
   return hipGetLastError();
 }
 
 template <int D, bool FP8, bool IND>
-static hipError_t launch_mb(const DecodeArgs& a, int mb, dim3 grid, hipStream_t st) {
+static hipError_t launch_mb(const DecodeArgs& a, int mb, dim3 grid, hipStream_t st, hipEvent_t ev0,
+                            hipEvent_t ev1) {
   switch (mb) {
-    case 1: return launch_partial_t<D, FP8, IND, 1>(a, grid, st);
-    case 2: return launch_partial_t<D, FP8, IND, 2>(a, grid, st);
-    default: return launch_partial_t<D, FP8, IND, 4>(a, grid, st);
+    case 1: return launch_partial_t<D, FP8, IND, 1>(a, grid, st, ev0, ev1);
+    case 2: return launch_partial_t<D, FP8, IND, 2>(a, grid, st, ev0, ev1);
+    default: return launch_partial_t<D, FP8, IND, 4>(a, grid, st, ev0, ev1);
   }
 }
 
 size_t partial_lds_bytes(int D, bool fp8, bool indirect, int chunk) {
-  return (size_t)kWaves * wave_tile_bytes(D, fp8) + 2 * kWaves * 16 * 4 + table_bytes(indirect, chunk);
+  return (size_t)kPWaves * wave_tile_bytes(D, fp8) + 2 * kPWaves * 16 * 4 + table_bytes(indirect, chunk);
 }
 
 hipError_t launch_partial(const DecodeArgs& a, int D, bool fp8, bool indirect, int mb, dim3 grid,
-                          hipStream_t st) {
+                          hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   if (D == 128) {
-    if (fp8) return indirect ? launch_mb<128, true, true>(a, mb, grid, st) : launch_mb<128, true, false>(a, mb, grid, st);
-    return indirect ? launch_mb<128, false, true>(a, mb, grid, st) : launch_mb<128, false, false>(a, mb, grid, st);
+    if (fp8)
+      return indirect ? launch_mb<128, true, true>(a, mb, grid, st, ev0, ev1)
+                      : launch_mb<128, true, false>(a, mb, grid, st, ev0, ev1);
+    return indirect ? launch_mb<128, false, true>(a, mb, grid, st, ev0, ev1)
+                    : launch_mb<128, false, false>(a, mb, grid, st, ev0, ev1);
   }
-  if (fp8) return indirect ? launch_mb<64, true, true>(a, mb, grid, st) : launch_mb<64, true, false>(a, mb, grid, st);
-  return indirect ? launch_mb<64, false, true>(a, mb, grid, st) : launch_mb<64, false, false>(a, mb, grid, st);
+  if (fp8)
+    return indirect ? launch_mb<64, true, true>(a, mb, grid, st, ev0, ev1)
+                    : launch_mb<64, true, false>(a, mb, grid, st, ev0, ev1);
+  return indirect ? launch_mb<64, false, true>(a, mb, grid, st, ev0, ev1)
+                  : launch_mb<64, false, false>(a, mb, grid, st, ev0, ev1);
 }
 
 hipError_t launch_combine(const DecodeArgs& a, int D, dim3 grid, hipStream_t st) {

@@ -98,8 +98,9 @@ typedef struct gqa_decode_params {
                                 else a multiple of 32 (at most 4096 for paged or top-K) */
   int32_t num_cus;           /* compute units to plan for; 0 = ask the current device   */
   int32_t reserved0;
-  /* Optional timing hooks: hipEvent_t handles recorded on `stream` right
-   * before and right after the split-KV partial kernel.  NULL = not used.  */
+  /* Optional timing hooks: hipEvent_t handles that the split-KV partial
+   * kernel's dispatch stamps when the kernel starts and when it ends (so
+   * their elapsed time is the kernel alone).  NULL = not used.            */
   void* partial_event_begin;
   void* partial_event_end;
 } gqa_decode_params;

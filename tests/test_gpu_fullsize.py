@@ -1,0 +1,61 @@
+"""The six named workloads at full size on the GPU, in the planner's default
+launch configuration (the one bench.py times), checked against the fp64
+oracle on a seeded sample of output rows computed one by one.  Needs a
+gfx950 GPU; the largest (paged, 4 GiB of K/V) takes about a minute.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import gqa_inputs as gi
+from gpu_common import Uploaded, compare, log, oracle
+
+pytestmark = pytest.mark.gpu
+
+SAMPLE_ROWS = 48
+
+
+def _sample_rows(w, k, seed):
+    s = w.spec
+    rng = np.random.default_rng(seed)
+    rows = set()
+    # always include the first and last query head of the first and last request
+    for b in (0, s.batch - 1):
+        for h in (0, s.h_q - 1):
+            rows.add((b, s.s_q - 1, h))
+    while len(rows) < min(k, s.batch * s.s_q * s.h_q):
+        rows.add((int(rng.integers(s.batch)), int(rng.integers(s.s_q)), int(rng.integers(s.h_q))))
+    return sorted(rows)
+
+
+@pytest.mark.parametrize("name", ["tiny", "long128k", "ragged", "ragged_sq8", "paged", "sparse_fp8"])
+def test_named_workload_full_size(name):
+    log(f"[fullsize] {name}: generating")
+    w = gi.named(name)
+    up = Uploaded(w)
+    log(f"[fullsize] {name}: plan {up.plan}")
+    up.run()
+    O, LSE = up.result()
+    rows = _sample_rows(w, SAMPLE_ROWS, seed=len(name))
+    Oref, Lref = oracle(w, gate_mode=up.gate_mode, rows=rows)
+    idx_b = np.array([r[0] for r in rows])
+    idx_i = np.array([r[1] for r in rows])
+    idx_h = np.array([r[2] for r in rows])
+    stats = compare(O[idx_b, idx_i, idx_h], LSE[idx_b, idx_h, idx_i], Oref[idx_b, idx_i, idx_h],
+                    Lref[idx_b, idx_h, idx_i], fp8=w.spec.kv_dtype == gi.KV_FP8, label=f"{name} (sampled)")
+    # Properties of every row at any size: finite, and each output is a
+    # convex combination of V rows (times a sigmoid <= 1), so |O| never
+    # exceeds the largest |V| of its KV head and column (plus bf16 rounding).
+    assert np.isfinite(O).all() and np.isfinite(LSE).all()
+    s = w.spec
+    G_ = s.h_q // s.h_kv
+    if s.kv_dtype == gi.KV_FP8:
+        bound = np.full((s.batch, s.h_kv, s.head_dim), 448.0) * w.v_scale[:, :, None]
+    else:
+        vmax = up.v.reshape(-1, s.h_kv, s.head_dim).float().abs().amax(dim=0).cpu().numpy()
+        bound = np.broadcast_to(vmax[None], (s.batch, s.h_kv, s.head_dim))
+    bound_q = np.repeat(bound, G_, axis=1)[:, None, :, :]          # [B, 1, H_q, d]
+    assert (np.abs(O) <= bound_q * (1 + 2 ** -8) + 1e-6).all(), f"{name}: |O| exceeds max |V|"
+    del up
+    torch.cuda.empty_cache()
