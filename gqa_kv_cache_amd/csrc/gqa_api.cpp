@@ -17,8 +17,8 @@
 #include "gqa_device.h"
 
 namespace gqa {
-hipError_t launch_partial(const DecodeArgs& a, int D, bool fp8, bool indirect, int mb, dim3 grid,
-                          hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
+hipError_t launch_partial(const DecodeArgs& a, int D, bool fp8, int mode, int mb, dim3 grid, hipStream_t st,
+                          hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_combine(const DecodeArgs& a, int D, dim3 grid, hipStream_t st);
 hipError_t launch_resolve(const DecodeArgs& a, int64_t* out, int list_cap, hipStream_t st);
 size_t partial_lds_bytes(int D, bool fp8, bool indirect, int chunk);
@@ -125,6 +125,21 @@ gqa_status check_shape(const gqa_decode_params* p) {
   return GQA_OK;
 }
 
+// A ragged cache without a top-K list is split into equal chunks of packed
+// rows (each chunk cut at request boundaries inside the kernel) instead of
+// per-request chunks: every workgroup then streams the same number of rows
+// whatever the mix of lengths.
+bool packed_mode(const gqa_decode_params* p) { return p->layout == GQA_LAYOUT_RAGGED && p->topk == 0; }
+
+// Bytes of the fp32 partial outputs (the LSE partials follow, rounded up to
+// 256 bytes): (request, KV head, split) slots of rows x head_dim each; packed
+// chunks use slots (request + chunk, KV head).
+size_t partial_o_bytes(const gqa_decode_params* p, const gqa_decode_plan& plan) {
+  const int64_t slots = packed_mode(p) ? ((int64_t)p->batch + plan.num_splits - 1) * p->h_kv
+                                       : (int64_t)p->batch * p->h_kv * plan.num_splits;
+  return (size_t)slots * plan.rows * p->head_dim * sizeof(float);
+}
+
 gqa_status make_plan(const gqa_decode_params* p, gqa_decode_plan* plan) {
   gqa_status st = check_shape(p);
   if (st != GQA_OK) return st;
@@ -133,25 +148,30 @@ gqa_status make_plan(const gqa_decode_params* p, gqa_decode_plan* plan) {
   plan->rows = rows;
   plan->row_blocks = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
   const bool indirect = p->layout == GQA_LAYOUT_PAGED || p->topk > 0;
+  const bool packed = packed_mode(p);
   const int64_t L = p->topk > 0 ? p->topk : p->max_seqlen_kv;
   const int64_t pairs = (int64_t)p->batch * p->h_kv;
   const int hpw = heads_per_wg(p->h_kv);
+  const int64_t groups = p->h_kv / hpw;
   int64_t chunk = p->kv_chunk;
   if (chunk == 0) {
     int cus = p->num_cus ? p->num_cus : device_cus();
     if (cus <= 0) return fail(GQA_ERR_HIP, "cannot query the device's compute-unit count");
-    // A workgroup covers hpw heads x chunk list positions.  Aim for about
-    // one workgroup per CU over the whole grid (MI355X measurements: one
-    // resident round of long workgroups streams best and writes the fewest
-    // partials), with 128..2048 positions per workgroup and never more than
-    // the list.  A ragged batch whose lengths vary (its packed cache holds
-    // fewer than batch * max_seqlen_kv rows) takes at most 1024 so that
-    // requests of very different lengths still balance across CUs.
-    const int64_t per = cdiv(std::max<int64_t>(pairs * L, 1), (int64_t)cus * hpw);
-    const bool varied = p->layout == GQA_LAYOUT_RAGGED && p->kv_rows < (int64_t)p->batch * p->max_seqlen_kv;
-    chunk = round_up(std::max<int64_t>(per, 128), 128);
-    chunk = std::min<int64_t>(chunk, varied ? 1024 : 4096);
-    chunk = std::min<int64_t>(chunk, round_up(std::max<int64_t>(L, 1), 32));
+    if (packed) {
+      // One workgroup per CU over the packed rows, each the same size.
+      const int64_t per = cdiv(p->kv_rows * groups, cus);
+      chunk = std::min<int64_t>(round_up(std::max<int64_t>(per, 64), 32), 1 << 24);
+    } else {
+      // A workgroup covers hpw heads x chunk list positions.  Aim for about
+      // one workgroup per CU over the whole grid (MI355X measurements: one
+      // resident round of long workgroups streams best and writes the
+      // fewest partials), with 128..4096 positions per workgroup and never
+      // more than the list.
+      const int64_t per = cdiv(std::max<int64_t>(pairs * L, 1), (int64_t)cus * hpw);
+      chunk = round_up(std::max<int64_t>(per, 128), 128);
+      chunk = std::min<int64_t>(chunk, 4096);
+      chunk = std::min<int64_t>(chunk, round_up(std::max<int64_t>(L, 1), 32));
+    }
   }
   // Shared memory of one partial workgroup (per-wave K/V tiles plus the
   // row table of paged / top-K chunks) must fit a workgroup's LDS.
@@ -159,15 +179,17 @@ gqa_status make_plan(const gqa_decode_params* p, gqa_decode_plan* plan) {
   if (lds > kMaxLdsPerWorkgroup)
     return fail(GQA_ERR_UNSUPPORTED, "kv_chunk %lld needs %zu bytes of LDS per workgroup (limit %zu)",
                 (long long)chunk, lds, kMaxLdsPerWorkgroup);
-  const int64_t splits = std::max<int64_t>(1, cdiv(L, chunk));
+  const int64_t splits = packed ? cdiv(p->kv_rows, chunk) : std::max<int64_t>(1, cdiv(L, chunk));
   if (splits > INT32_MAX) return fail(GQA_ERR_UNSUPPORTED, "too many splits");
   plan->kv_chunk = (int32_t)chunk;
   plan->num_splits = (int32_t)splits;
-  plan->partial_workgroups = (pairs / hpw) * splits;
-  plan->combine = splits > 1 ? 1 : 0;
-  if (splits > 1) {
-    const size_t opart = (size_t)pairs * splits * rows * p->head_dim * sizeof(float);
-    const size_t lpart = (size_t)pairs * splits * rows * sizeof(float);
+  plan->partial_workgroups = groups * splits * (packed ? 1 : p->batch);
+  // Packed: requests that span chunks are merged by the combine, which
+  // also writes the empty requests; partial slots are (request + chunk).
+  plan->combine = (packed || splits > 1) ? 1 : 0;
+  if (plan->combine) {
+    const size_t opart = partial_o_bytes(p, *plan);
+    const size_t lpart = opart / p->head_dim;
     plan->workspace_bytes = round_up(opart, 256) + round_up(lpart, 256);
   }
   return GQA_OK;
@@ -197,6 +219,16 @@ void fill_args(gqa::DecodeArgs& a, const gqa_decode_params* p, const gqa_decode_
   a.chunk = plan.kv_chunk;
   a.num_splits = plan.num_splits;
   a.heads_per_wg = heads_per_wg(p->h_kv);
+  a.packed = packed_mode(p) ? 1 : 0;
+  if (a.packed) {
+    a.part_sb = (int64_t)p->h_kv * plan.rows;
+    a.part_sg = plan.rows;
+    a.part_ss = (int64_t)p->h_kv * plan.rows;
+  } else {
+    a.part_sb = (int64_t)p->h_kv * plan.num_splits * plan.rows;
+    a.part_sg = (int64_t)plan.num_splits * plan.rows;
+    a.part_ss = plan.rows;
+  }
   const float scale = p->softmax_scale != 0.f ? p->softmax_scale : 1.0f / std::sqrt((float)p->head_dim);
   a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
 }
@@ -286,15 +318,16 @@ gqa_status gqa_decode_run(const gqa_decode_params* p, const void* q, const void*
   a.o = static_cast<uint16_t*>(o);
   a.lse = lse;
   if (plan.workspace_bytes > 0) {
-    const size_t opart = (size_t)p->batch * p->h_kv * plan.num_splits * plan.rows * p->head_dim * sizeof(float);
     a.o_part = static_cast<float*>(workspace);
-    a.lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + round_up(opart, 256));
+    a.lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + round_up(partial_o_bytes(p, plan), 256));
   }
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool indirect = p->layout == GQA_LAYOUT_PAGED || p->topk > 0;
-  const dim3 grid(plan.num_splits, p->h_kv / heads_per_wg(p->h_kv), p->batch);
-  hipError_t e = gqa::launch_partial(a, p->head_dim, p->kv_dtype == GQA_KV_FP8_E4M3FN, indirect, plan.row_blocks,
+  const int mode = a.packed ? 2 : (indirect ? 1 : 0);
+  // Packed chunks span requests: one grid row covers the whole batch.
+  const dim3 grid(plan.num_splits, p->h_kv / heads_per_wg(p->h_kv), a.packed ? 1 : p->batch);
+  hipError_t e = gqa::launch_partial(a, p->head_dim, p->kv_dtype == GQA_KV_FP8_E4M3FN, mode, plan.row_blocks,
                                      grid, s, static_cast<hipEvent_t>(p->partial_event_begin),
                                      static_cast<hipEvent_t>(p->partial_event_end));
   if (e != hipSuccess) return hip_fail(e, "partial kernel launch");

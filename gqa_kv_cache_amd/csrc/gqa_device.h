@@ -46,14 +46,18 @@ struct DecodeArgs {
   const uint16_t* gate;       // bf16
   uint16_t* o;                // bf16 [B, S_q, H_q, D]
   float* lse;                 // fp32 [B, H_q, S_q]
-  float* o_part;              // fp32 [B, H_kv, splits, rows, D]
-  float* lse_part;            // fp32 [B, H_kv, splits, rows], base-2
+  float* o_part;              // fp32 partial rows x D (row index below)
+  float* lse_part;            // fp32 partial rows, base-2
+  // Partial row of (request b, KV head g, split s, query row r):
+  // b * part_sb + g * part_sg + s * part_ss + r.
+  int64_t part_sb, part_sg, part_ss;
   int64_t kv_rows;
   int32_t batch, s_q, h_q, h_kv, group, rows;
   int32_t layout, causal, max_seqlen, seq_cap;
   int32_t page_shift, max_pages, topk_len, gate_mode;
   int32_t chunk, num_splits;
   int32_t heads_per_wg;       // KV heads one partial workgroup covers (1, 2 or 4)
+  int32_t packed;             // 1: ragged cache split into equal row chunks (split s = chunk s)
   float scale_log2;           // softmax scale * log2(e)
 };
 
@@ -83,6 +87,24 @@ __device__ __forceinline__ int64_t row_base(const DecodeArgs& a, int b) {
 __device__ __forceinline__ int slot_token(const DecodeArgs& a, int b, int n, int p) {
   int t = (a.topk_len > 0) ? a.topk[(int64_t)b * a.topk_len + p] : p;
   return (t >= 0 && t < n) ? t : -1;
+}
+
+// Packed ragged cache: the request whose rows hold packed row x, i.e. the
+// largest b < batch with cu_seqlens[b] <= x (0 if there is none), found by a
+// 64-way search with one wave's lanes (one ballot per round, at most three
+// rounds for 65535 requests).  Every lane gets the same result.  With
+// offsets that decrease the result is some b in [0, batch).
+__device__ __forceinline__ int packed_request(const DecodeArgs& a, int64_t x, int lane) {
+  int lo = 0, hi = a.batch;
+  while (hi - lo > 1) {
+    const int step = (hi - lo + 63) / 64;
+    const int idx = lo + lane * step;
+    const bool le = idx < hi && (int64_t)a.cu_seqlens[idx] <= x;
+    const int cnt = __popcll(__ballot(le));
+    lo += max(cnt - 1, 0) * step;
+    hi = min(lo + step, hi);
+  }
+  return lo;
 }
 
 // Contiguous / ragged layouts: the same row as token_row, without the

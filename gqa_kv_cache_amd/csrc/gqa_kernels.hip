@@ -89,10 +89,26 @@ __device__ __forceinline__ int vblk(int blk, int tok) {
   return D == 128 ? (blk ^ (tok & 7)) : (blk ^ ((tok >> 1) & 3));
 }
 
-template <int D, bool FP8, bool INDIRECT, int MB>
-__global__ void __launch_bounds__(kPThreads, MB == 1 ? 2 : 1) gqa_partial_kernel(DecodeArgs a) {
+// How a partial workgroup finds its work.
+//   kDense    one chunk of one request's list (contiguous / ragged cache),
+//             addresses computed from the position;
+//   kIndirect the same through a block table and / or a top-K list, resolved
+//             into an LDS row table first;
+//   kPacked   one chunk of the packed rows of a ragged cache: the chunk is cut
+//             at request boundaries into segments, each computed like a
+//             kDense chunk of its request.  Every workgroup then gets the same
+//             number of rows, however the lengths vary.
+constexpr int kDense = 0, kIndirect = 1, kPacked = 2;
+
+// Two resident workgroups per CU for one 16-row block, except in the packed
+// mode, whose grid is planned as one workgroup per CU: there the whole
+// register file is the kernel's.
+template <int D, bool FP8, int MODE, int MB>
+__global__ void __launch_bounds__(kPThreads, (MB == 1 && MODE != kPacked) ? 2 : 1) gqa_partial_kernel(DecodeArgs a) {
   using TS = TileShape<D, FP8>;
   constexpr int RB = TS::RB, CPR = TS::CPR, TPI = TS::TPI, NLD = TS::NLD, KK = TS::KK, NB = TS::NB;
+  constexpr bool INDIRECT = MODE == kIndirect;
+  constexpr bool PACKED = MODE == kPacked;
   static_assert(kPWaves * 16 * D * 4 <= kPWaves * wave_tile_bytes(D, FP8), "accumulators fit in the tiles");
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -109,15 +125,44 @@ __global__ void __launch_bounds__(kPThreads, MB == 1 ? 2 : 1) gqa_partial_kernel
   const int wph = kPWaves / hpw;                 // waves per head
   const int hs = wave % hpw;                    // head slot of this wave
   const int sub = wave / hpw;                   // this wave's share of the head's tiles
-  const int split = blockIdx.x, b = blockIdx.z;
   const int g0 = blockIdx.y * hpw;
   const int g = g0 + hs;
+  const int split = blockIdx.x;
 
-  const int n = seq_len(a, b);
-  const int L = list_len(a, n);
-  const int start = split * a.chunk;
-  if (a.num_splits > 1 && start >= L) return;  // nothing in this split; the combine skips it
-  const int end = min(L, start + a.chunk);
+  // Packed rows [x0, x1) of this workgroup and the first request they meet.
+  int64_t x0 = 0, x1 = 0;
+  int bnext = 0;
+  if constexpr (PACKED) {
+    x0 = (int64_t)split * a.chunk;
+    x1 = x0 + a.chunk;
+    bnext = __builtin_amdgcn_readfirstlane(packed_request(a, x0, lane));
+  }
+
+  // One pass per segment: list positions [start, end) of request b, written
+  // as partial `split` of b, or as the final output when the segment is b's
+  // whole list (fin).  Only the packed mode has more than one.
+  for (;;) {
+  int b, n, start, end;
+  bool fin;
+  if constexpr (PACKED) {
+    if (bnext >= a.batch) break;
+    const int64_t s0 = __builtin_amdgcn_readfirstlane(a.cu_seqlens[bnext]);
+    if (s0 >= x1) break;
+    b = bnext++;
+    n = __builtin_amdgcn_readfirstlane(seq_len(a, b));
+    start = (int)min<int64_t>(max<int64_t>(x0 - s0, 0), n);
+    end = (int)max<int64_t>(min<int64_t>(x1 - s0, n), 0);
+    if (start >= end) continue;
+    fin = (start == 0 && end == n);
+  } else {
+    b = blockIdx.z;
+    n = seq_len(a, b);
+    const int L = list_len(a, n);
+    start = split * a.chunk;
+    if (a.num_splits > 1 && start >= L) return;  // nothing in this split; the combine skips it
+    end = min(L, start + a.chunk);
+    fin = (a.num_splits == 1);
+  }
   const int ntiles = end > start ? (end - start + kTile - 1) / kTile : 0;
   const int64_t base = row_base(a, b);
 
@@ -419,7 +464,7 @@ __global__ void __launch_bounds__(kPThreads, MB == 1 ? 2 : 1) gqa_partial_kernel
   float* wacc = reinterpret_cast<float*>(tiles);
   float* wm = wstat;
   float* wl = wstat + kPWaves * 16;
-  const bool final_out = (a.num_splits == 1);
+  const bool final_out = fin;
   constexpr int D8 = D / 8;
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
@@ -490,13 +535,16 @@ __global__ void __launch_bounds__(kPThreads, MB == 1 ? 2 : 1) gqa_partial_kernel
         *reinterpret_cast<u32x4*>(a.o + oidx) = ov;
         if (d8 == 0) a.lse[((int64_t)b * a.h_q + h) * a.s_q + i] = lse2 * 0.69314718055994530942f;
       } else {
-        const int64_t prow = ((int64_t)(b * a.h_kv + gg) * a.num_splits + split) * a.rows + r;
+        const int64_t prow = b * a.part_sb + gg * a.part_sg + split * a.part_ss + r;
         float* dst = a.o_part + prow * D + d8 * 8;
         *reinterpret_cast<f32x4*>(dst) = f32x4{o[0], o[1], o[2], o[3]};
         *reinterpret_cast<f32x4*>(dst + 4) = f32x4{o[4], o[5], o[6], o[7]};
         if (d8 == 0) a.lse_part[prow] = lse2;
       }
     }
+  }
+  if constexpr (!PACKED) break;
+  __syncthreads();  // the next segment stages tiles where the merge just read
   }
 }
 
@@ -515,11 +563,22 @@ __global__ void __launch_bounds__(kThreads) gqa_combine_kernel(DecodeArgs a) {
   __shared__ float rm[SG], rl[SG];
   const int r = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int n = seq_len(a, b);
-  const int L = list_len(a, n);
-  const int nsp = min(a.num_splits, (L + a.chunk - 1) / a.chunk);
-  const int64_t first = (int64_t)(b * a.h_kv + g) * a.num_splits;
-  const float* lsep = a.lse_part + first * a.rows + r;
-  const float* op = a.o_part + (first * a.rows + r) * D;
+  // Splits [s_lo, s_lo + nsp) of request b.  Packed: the chunks its rows
+  // meet; a request inside one chunk was finished by the partial kernel.
+  int s_lo = 0, nsp;
+  if (a.packed) {
+    const int64_t r0 = a.cu_seqlens[b];
+    const int64_t w0 = r0 >= 0 ? r0 / a.chunk : 0;
+    const int64_t w1 = r0 >= 0 ? (r0 + n - 1) / a.chunk : 0;
+    if (n > 0 && r0 >= 0 && w0 == w1 && w0 < a.num_splits) return;
+    s_lo = (int)min<int64_t>(w0, a.num_splits - 1);
+    nsp = n > 0 ? (int)(min<int64_t>(max<int64_t>(w1, w0), a.num_splits - 1) - s_lo + 1) : 0;
+  } else {
+    nsp = min(a.num_splits, (list_len(a, n) + a.chunk - 1) / a.chunk);
+  }
+  const int64_t first = b * a.part_sb + g * a.part_sg + s_lo * a.part_ss + r;
+  const float* lsep = a.lse_part + first;
+  const float* op = a.o_part + first * D;
   const int d4 = threadIdx.x % Q4;
   const int sg = threadIdx.x / Q4;
 
@@ -530,9 +589,9 @@ __global__ void __launch_bounds__(kThreads) gqa_combine_kernel(DecodeArgs a) {
     f32x4 x[UNROLL];
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
-      const int sidx = min(s0 + u * SG, nsp - 1);
-      ls[u] = lsep[(int64_t)sidx * a.rows];
-      x[u] = *reinterpret_cast<const f32x4*>(op + (int64_t)sidx * a.rows * D + d4 * 4);
+      const int64_t sidx = min(s0 + u * SG, nsp - 1);
+      ls[u] = lsep[sidx * a.part_ss];
+      x[u] = *reinterpret_cast<const f32x4*>(op + sidx * a.part_ss * D + d4 * 4);
     }
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u)
@@ -619,21 +678,31 @@ __global__ void __launch_bounds__(kThreads) gqa_resolve_kernel(DecodeArgs a, int
 
 // ev0 / ev1 (may be null): events stamped by the dispatch itself at the
 // kernel's start and end, so they time the kernel alone.
-template <int D, bool FP8, bool IND, int MB>
+template <int D, bool FP8, int MODE, int MB>
 static hipError_t launch_partial_t(const DecodeArgs& a, dim3 grid, hipStream_t st, hipEvent_t ev0,
                                    hipEvent_t ev1) {
-  const size_t lds = table_bytes(IND, a.chunk);
-  hipExtLaunchKernelGGL((gqa_partial_kernel<D, FP8, IND, MB>), grid, dim3(kPThreads), lds, st, ev0, ev1, 0, a);
+  const size_t lds = table_bytes(MODE == kIndirect, a.chunk);
+  hipExtLaunchKernelGGL((gqa_partial_kernel<D, FP8, MODE, MB>), grid, dim3(kPThreads), lds, st, ev0, ev1, 0, a);
   return hipGetLastError();
 }
 
-template <int D, bool FP8, bool IND>
+template <int D, bool FP8, int MODE>
 static hipError_t launch_mb(const DecodeArgs& a, int mb, dim3 grid, hipStream_t st, hipEvent_t ev0,
                             hipEvent_t ev1) {
   switch (mb) {
-    case 1: return launch_partial_t<D, FP8, IND, 1>(a, grid, st, ev0, ev1);
-    case 2: return launch_partial_t<D, FP8, IND, 2>(a, grid, st, ev0, ev1);
-    default: return launch_partial_t<D, FP8, IND, 4>(a, grid, st, ev0, ev1);
+    case 1: return launch_partial_t<D, FP8, MODE, 1>(a, grid, st, ev0, ev1);
+    case 2: return launch_partial_t<D, FP8, MODE, 2>(a, grid, st, ev0, ev1);
+    default: return launch_partial_t<D, FP8, MODE, 4>(a, grid, st, ev0, ev1);
+  }
+}
+
+template <int D, bool FP8>
+static hipError_t launch_mode(const DecodeArgs& a, int mode, int mb, dim3 grid, hipStream_t st, hipEvent_t ev0,
+                              hipEvent_t ev1) {
+  switch (mode) {
+    case kIndirect: return launch_mb<D, FP8, kIndirect>(a, mb, grid, st, ev0, ev1);
+    case kPacked: return launch_mb<D, FP8, kPacked>(a, mb, grid, st, ev0, ev1);
+    default: return launch_mb<D, FP8, kDense>(a, mb, grid, st, ev0, ev1);
   }
 }
 
@@ -641,20 +710,14 @@ size_t partial_lds_bytes(int D, bool fp8, bool indirect, int chunk) {
   return (size_t)kPWaves * wave_tile_bytes(D, fp8) + 2 * kPWaves * 16 * 4 + table_bytes(indirect, chunk);
 }
 
-hipError_t launch_partial(const DecodeArgs& a, int D, bool fp8, bool indirect, int mb, dim3 grid,
-                          hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
-  if (D == 128) {
-    if (fp8)
-      return indirect ? launch_mb<128, true, true>(a, mb, grid, st, ev0, ev1)
-                      : launch_mb<128, true, false>(a, mb, grid, st, ev0, ev1);
-    return indirect ? launch_mb<128, false, true>(a, mb, grid, st, ev0, ev1)
-                    : launch_mb<128, false, false>(a, mb, grid, st, ev0, ev1);
-  }
-  if (fp8)
-    return indirect ? launch_mb<64, true, true>(a, mb, grid, st, ev0, ev1)
-                    : launch_mb<64, true, false>(a, mb, grid, st, ev0, ev1);
-  return indirect ? launch_mb<64, false, true>(a, mb, grid, st, ev0, ev1)
-                  : launch_mb<64, false, false>(a, mb, grid, st, ev0, ev1);
+// mode: 0 dense, 1 indirect (paged / top-K), 2 packed ragged.
+hipError_t launch_partial(const DecodeArgs& a, int D, bool fp8, int mode, int mb, dim3 grid, hipStream_t st,
+                          hipEvent_t ev0, hipEvent_t ev1) {
+  if (D == 128)
+    return fp8 ? launch_mode<128, true>(a, mode, mb, grid, st, ev0, ev1)
+               : launch_mode<128, false>(a, mode, mb, grid, st, ev0, ev1);
+  return fp8 ? launch_mode<64, true>(a, mode, mb, grid, st, ev0, ev1)
+             : launch_mode<64, false>(a, mode, mb, grid, st, ev0, ev1);
 }
 
 hipError_t launch_combine(const DecodeArgs& a, int D, dim3 grid, hipStream_t st) {

@@ -78,6 +78,61 @@ def test_ragged_seeded_lengths():
     check_workload(w, label="ragged U[1,3000]")
 
 
+# A ragged cache without top-K is cut into equal chunks of packed rows, each
+# split at request boundaries.  With 32- and 64-row chunks these lengths put
+# several requests (and empty ones) inside one chunk, requests that start or
+# end exactly on a chunk boundary, and requests over many chunks.
+PACKED_LENGTHS = (5, 0, 40, 1, 0, 0, 77, 32, 31, 33, 64, 3, 0, 128, 64, 0, 500, 2)
+
+
+@pytest.mark.parametrize("chunk", [32, 64, 96])
+def test_packed_ragged_segments(chunk):
+    s = spec(layout="ragged", h_q=32, h_kv=8, fixed_lengths=PACKED_LENGTHS)
+    check_workload(gi.build(s, seed=40 + chunk), kv_chunk=chunk, label=f"packed segments, chunk {chunk}")
+
+
+@pytest.mark.parametrize("chunk", [32, 64])
+def test_packed_ragged_causal_multi_token(chunk):
+    s = spec(layout="ragged", h_q=16, h_kv=4, s_q=4, causal=True, fixed_lengths=(3, 64, 0, 65, 200, 4))
+    check_workload(gi.build(s, seed=50 + chunk), kv_chunk=chunk, label=f"packed causal S_q=4, chunk {chunk}")
+
+
+def test_packed_ragged_all_empty():
+    s = spec(layout="ragged", h_q=8, h_kv=2, fixed_lengths=(0, 0, 0))
+    check_workload(gi.build(s, seed=61), label="packed, every request empty")
+
+
+@pytest.mark.parametrize("chunk", [0, 64])
+def test_packed_ragged_offset_and_slack(chunk):
+    """Packed rows that start after row 0 and a cache with unused rows at
+    both ends: offsets are taken as given, and the unused rows are read by
+    no request (they hold large values that would show if they were)."""
+    s = spec(layout="ragged", h_q=32, h_kv=8, fixed_lengths=(70, 0, 1, 300, 33))
+    w = gi.build(s, seed=62)
+    head, tail = 45, 130
+    pad = lambda c, n: np.full((n,) + c.shape[1:], 0x4480, dtype=c.dtype)   # bf16 1024.0
+    w2 = dataclasses.replace(
+        w, k_cache=np.concatenate([pad(w.k_cache, head), w.k_cache, pad(w.k_cache, tail)]),
+        v_cache=np.concatenate([pad(w.v_cache, head), w.v_cache, pad(w.v_cache, tail)]),
+        cu_seqlens=(w.cu_seqlens + head).astype(np.int32))
+    check_workload(w2, kv_chunk=chunk, label=f"packed offset + slack, chunk {chunk}")
+
+
+@pytest.mark.parametrize("chunk", [32, 128])
+def test_packed_ragged_fp8(chunk):
+    s = spec(layout="ragged", h_q=32, h_kv=8, kv_dtype=gi.KV_FP8, gate=True,
+             fixed_lengths=(100, 0, 31, 257, 1))
+    check_workload(gi.build(s, seed=70 + chunk), kv_chunk=chunk, label=f"packed fp8 gated, chunk {chunk}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_packed_ragged_d64_one_head_group(d):
+    # H_kv = 1 (one head per workgroup) and H_kv = 2 (two)
+    for hkv in (1, 2):
+        s = spec(layout="ragged", h_q=8, h_kv=hkv, head_dim=d, fixed_lengths=(40, 0, 129, 7))
+        check_workload(gi.build(s, seed=80 + hkv), kv_chunk=32, label=f"packed d={d} h_kv={hkv}")
+
+
 def test_contiguous_capacity_larger_than_lengths():
     w = gi.build(spec(h_q=16, h_kv=2, fixed_lengths=(10, 200, 0), capacity=300), seed=9)
     check_workload(w, label="capacity 300")
