@@ -100,11 +100,16 @@ __device__ __forceinline__ int vblk(int blk, int tok) {
 //             number of rows, however the lengths vary.
 constexpr int kDense = 0, kIndirect = 1, kPacked = 2;
 
-// Two resident workgroups per CU for one 16-row block, except in the packed
-// mode, whose grid is planned as one workgroup per CU: there the whole
-// register file is the kernel's.
+// Resident workgroups per CU the register budget is sized for: two for one
+// 16-row block of FP8 or d = 64 tiles; one (the whole register file) for
+// bf16 d = 128, whose two register buffers of whole-row loads alone take
+// 128 VGPRs -- squeezed into half the file it spills, and every spill
+// reload waits for all loads in flight.
+template <int D, bool FP8, int MB>
+constexpr int partial_min_blocks() { return (MB == 1 && (FP8 || D == 64)) ? 2 : 1; }
+
 template <int D, bool FP8, int MODE, int MB>
-__global__ void __launch_bounds__(kPThreads, (MB == 1 && MODE != kPacked) ? 2 : 1) gqa_partial_kernel(DecodeArgs a) {
+__global__ void __launch_bounds__(kPThreads, (partial_min_blocks<D, FP8, MB>())) gqa_partial_kernel(DecodeArgs a) {
   using TS = TileShape<D, FP8>;
   constexpr int RB = TS::RB, CPR = TS::CPR, TPI = TS::TPI, NLD = TS::NLD, KK = TS::KK, NB = TS::NB;
   constexpr bool INDIRECT = MODE == kIndirect;
@@ -417,8 +422,12 @@ __global__ void __launch_bounds__(kPThreads, (MB == 1 && MODE != kPacked) ? 2 : 
   // LDS, at once refills the same registers with the tile two steps ahead
   // (a dummy past the end), then computes from LDS -- so two tiles of loads
   // are in flight while a tile is computed.  Every step is one straight-line
-  // block, so the compiler cannot hoist work above the loads and its waits
-  // leave the younger tile in flight.
+  // block, so the compiler cannot hoist work above the loads.  A pass takes
+  // two real tiles and the loop has one exit test: every path back to the
+  // loop head then has the same loads in flight (A older than B), which is
+  // what lets the compiler's counter waits keep the younger tile in flight
+  // (an exit between the two steps gives the loop a path on which A's
+  // loads are the youngest, and every pass then waits for all loads).
   {
     u32x4 kA[NLD], vA[NLD], kB[NLD], vB[NLD];
     int tile = sub;
@@ -428,7 +437,7 @@ __global__ void __launch_bounds__(kPThreads, (MB == 1 && MODE != kPacked) ? 2 : 
       const bool second = tile + wph < ntiles;
       load_tile(second ? tile + wph : tile, kB, vB, second);
       issue_fence();
-      while (true) {
+      while (tile + wph < ntiles) {  // A holds `tile`, B holds `tile + wph`, both real
         stage_tile(kA, vA);
         issue_fence();  // the staged registers are dead before they are refilled
         int ahead = tile + 2 * wph;
@@ -437,18 +446,21 @@ __global__ void __launch_bounds__(kPThreads, (MB == 1 && MODE != kPacked) ? 2 : 
         issue_fence();
         compute_tile(tile);
         issue_fence();
-        tile += wph;
-        if (tile >= ntiles) break;
         stage_tile(kB, vB);
-        issue_fence();  // the staged registers are dead before they are refilled
-        ahead = tile + 2 * wph;
+        issue_fence();
+        ahead = tile + 3 * wph;
         real = ahead < ntiles;
         load_tile(real ? ahead : tile, kB, vB, real);
         issue_fence();
+        compute_tile(tile + wph);
+        issue_fence();
+        tile += 2 * wph;
+      }
+      if (tile < ntiles) {  // an odd last tile, in A (B holds a dummy)
+        stage_tile(kA, vA);
+        issue_fence();
         compute_tile(tile);
         issue_fence();
-        tile += wph;
-        if (tile >= ntiles) break;
       }
     }
   }
