@@ -150,6 +150,8 @@ def main():
     ap.add_argument("--workload", default="long128k",
                     choices=["tiny", "long128k", "ragged", "ragged_sq8", "paged", "sparse_fp8"])
     ap.add_argument("--kv-chunk", type=int, default=0, help="force list positions per workgroup")
+    ap.add_argument("--math", default="auto", choices=["auto", "mfma", "valu"],
+                    help="math path of the partial kernel (auto: the planner's measured choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold", action="store_true", help="also time single calls after a 1 GiB cache flush")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -204,7 +206,8 @@ def main():
                            layout=s.layout, kv_dtype=s.kv_dtype, causal=s.causal,
                            max_seqlen_kv=w.max_seqlen, seq_capacity=cap, kv_rows=kv_rows,
                            page_size=s.page_size, max_pages_per_seq=mpp, topk=s.topk,
-                           gate_mode="elementwise" if gate is not None else "none", kv_chunk=args.kv_chunk)
+                           gate_mode="elementwise" if gate is not None else "none", kv_chunk=args.kv_chunk,
+                           math=args.math)
     plan = G.gqa_decode_make_plan(params)
     ws = torch.empty(max(plan["workspace_bytes"], 16), dtype=torch.uint8, device=dev)
     o = torch.empty((s.batch, s.s_q, s.h_q, s.head_dim), dtype=torch.bfloat16, device=dev)
@@ -302,6 +305,7 @@ def main():
             "s_q": s.s_q, "kv_tokens": tokens, "layout": s.layout, "causal": s.causal, "topk": s.topk,
             "kv_dtype": s.kv_dtype, "gate": w.gate is not None, "seed": w.seed,
             "kv_chunk": plan["kv_chunk"], "num_splits": plan["num_splits"],
+            "math": {1: "mfma", 2: "valu"}[plan["math"]],
         },
         "us_per_call": round(us_per_call, 3),
         "min_bytes_per_call": min_bytes,

@@ -31,6 +31,7 @@ GATE_NONE, GATE_ELEMENTWISE, GATE_HEADWISE = 0, 1, 2
 LAYOUTS = {"contiguous": LAYOUT_CONTIGUOUS, "ragged": LAYOUT_RAGGED, "paged": LAYOUT_PAGED}
 KV_DTYPES = {"bf16": KV_BF16, "fp8_e4m3fn": KV_FP8_E4M3FN}
 GATE_MODES = {"none": GATE_NONE, "elementwise": GATE_ELEMENTWISE, "headwise": GATE_HEADWISE}
+MATH = {"auto": 0, "mfma": 1, "valu": 2}
 
 STATUS = {0: "GQA_OK", 1: "GQA_ERR_INVALID_ARG", 2: "GQA_ERR_UNSUPPORTED", 3: "GQA_ERR_ALIGNMENT",
           4: "GQA_ERR_WORKSPACE", 5: "GQA_ERR_HIP"}
@@ -50,7 +51,7 @@ class Params(ctypes.Structure):
         ("seq_capacity", ctypes.c_int32), ("kv_rows", ctypes.c_int64), ("page_size", ctypes.c_int32),
         ("max_pages_per_seq", ctypes.c_int32), ("topk", ctypes.c_int32), ("gate_mode", ctypes.c_int32),
         ("softmax_scale", ctypes.c_float), ("kv_chunk", ctypes.c_int32), ("num_cus", ctypes.c_int32),
-        ("reserved0", ctypes.c_int32), ("partial_event_begin", ctypes.c_void_p),
+        ("math", ctypes.c_int32), ("partial_event_begin", ctypes.c_void_p),
         ("partial_event_end", ctypes.c_void_p),
     ]
 
@@ -59,7 +60,7 @@ class Plan(ctypes.Structure):
     _fields_ = [
         ("rows", ctypes.c_int32), ("row_blocks", ctypes.c_int32), ("kv_chunk", ctypes.c_int32),
         ("num_splits", ctypes.c_int32), ("partial_workgroups", ctypes.c_int64),
-        ("combine", ctypes.c_int32), ("reserved0", ctypes.c_int32), ("workspace_bytes", ctypes.c_size_t),
+        ("combine", ctypes.c_int32), ("math", ctypes.c_int32), ("workspace_bytes", ctypes.c_size_t),
     ]
 
 
@@ -113,7 +114,7 @@ def make_params(*, batch: int, s_q: int, h_q: int, h_kv: int, head_dim: int,
                 max_seqlen_kv: int, seq_capacity: int = 0, kv_rows: int,
                 page_size: int = 16, max_pages_per_seq: int = 0, topk: int = 0,
                 gate_mode="none", softmax_scale: Optional[float] = None,
-                kv_chunk: int = 0, num_cus: int = 0) -> Params:
+                kv_chunk: int = 0, num_cus: int = 0, math="auto") -> Params:
     p = Params()
     p.batch, p.s_q, p.h_q, p.h_kv, p.head_dim = batch, s_q, h_q, h_kv, head_dim
     p.layout = LAYOUTS[layout] if isinstance(layout, str) else int(layout)
@@ -129,6 +130,7 @@ def make_params(*, batch: int, s_q: int, h_q: int, h_kv: int, head_dim: int,
     p.softmax_scale = 0.0 if softmax_scale is None else float(softmax_scale)
     p.kv_chunk = kv_chunk
     p.num_cus = num_cus
+    p.math = MATH[math] if isinstance(math, str) else int(math)
     return p
 
 

@@ -17,8 +17,8 @@
 #include "gqa_device.h"
 
 namespace gqa {
-hipError_t launch_partial(const DecodeArgs& a, int D, bool fp8, int mode, int mb, dim3 grid, hipStream_t st,
-                          hipEvent_t ev0, hipEvent_t ev1);
+hipError_t launch_partial(const DecodeArgs& a, int D, bool fp8, int mode, int mb, int rv, dim3 grid,
+                          hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_combine(const DecodeArgs& a, int D, dim3 grid, hipStream_t st);
 hipError_t launch_resolve(const DecodeArgs& a, int64_t* out, int list_cap, hipStream_t st);
 size_t partial_lds_bytes(int D, bool fp8, bool indirect, int chunk);
@@ -42,6 +42,7 @@ gqa_status fail(gqa_status s, const char* fmt, ...) {
 constexpr int kMaxChunkIndirect = 4096;
 constexpr size_t kMaxLdsPerWorkgroup = 160 * 1024;  // gfx950: 160 KiB of LDS per CU and workgroup
 constexpr int kMaxRows = 64;
+constexpr int kMaxValuRows = 8;
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -122,6 +123,10 @@ gqa_status check_shape(const gqa_decode_params* p) {
                   kMaxChunkIndirect);
   }
   if (p->num_cus < 0) return fail(GQA_ERR_INVALID_ARG, "num_cus %d < 0", p->num_cus);
+  if (p->math < GQA_MATH_AUTO || p->math > GQA_MATH_VALU) return fail(GQA_ERR_INVALID_ARG, "unknown math %d", p->math);
+  if (p->math == GQA_MATH_VALU && rows > kMaxValuRows)
+    return fail(GQA_ERR_UNSUPPORTED, "the VALU path takes at most %d query rows per KV head, not %lld", kMaxValuRows,
+                (long long)rows);
   return GQA_OK;
 }
 
@@ -140,13 +145,24 @@ size_t partial_o_bytes(const gqa_decode_params* p, const gqa_decode_plan& plan) 
   return (size_t)slots * plan.rows * p->head_dim * sizeof(float);
 }
 
+// The math path GQA_MATH_AUTO takes for a group of `rows` query rows.
+// Measured on MI355X over 128K-token decodes (bf16 d = 128 and 64, FP8
+// d = 128; three processes each): MFMA is 5-7 % faster from 2 rows up and
+// more than twice as fast at 8, its time flat from 1 to 16 rows; at 1 row
+// the VALU path is as fast or up to 1 % faster.
+int auto_math(int rows) { return rows == 1 ? GQA_MATH_VALU : GQA_MATH_MFMA; }
+
 gqa_status make_plan(const gqa_decode_params* p, gqa_decode_plan* plan) {
   gqa_status st = check_shape(p);
   if (st != GQA_OK) return st;
   std::memset(plan, 0, sizeof *plan);
   const int rows = (p->h_q / p->h_kv) * p->s_q;
   plan->rows = rows;
-  plan->row_blocks = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
+  plan->math = p->math == GQA_MATH_AUTO ? auto_math(rows) : p->math;
+  if (plan->math == GQA_MATH_VALU)
+    plan->row_blocks = rows <= 2 ? rows : (rows <= 4 ? 4 : 8);
+  else
+    plan->row_blocks = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
   const bool indirect = p->layout == GQA_LAYOUT_PAGED || p->topk > 0;
   const bool packed = packed_mode(p);
   const int64_t L = p->topk > 0 ? p->topk : p->max_seqlen_kv;
@@ -327,8 +343,10 @@ gqa_status gqa_decode_run(const gqa_decode_params* p, const void* q, const void*
   const int mode = a.packed ? 2 : (indirect ? 1 : 0);
   // Packed chunks span requests: one grid row covers the whole batch.
   const dim3 grid(plan.num_splits, p->h_kv / heads_per_wg(p->h_kv), a.packed ? 1 : p->batch);
-  hipError_t e = gqa::launch_partial(a, p->head_dim, p->kv_dtype == GQA_KV_FP8_E4M3FN, mode, plan.row_blocks,
-                                     grid, s, static_cast<hipEvent_t>(p->partial_event_begin),
+  const bool valu = plan.math == GQA_MATH_VALU;
+  hipError_t e = gqa::launch_partial(a, p->head_dim, p->kv_dtype == GQA_KV_FP8_E4M3FN, mode, valu ? 1 : plan.row_blocks,
+                                     valu ? plan.row_blocks : 0, grid, s,
+                                     static_cast<hipEvent_t>(p->partial_event_begin),
                                      static_cast<hipEvent_t>(p->partial_event_end));
   if (e != hipSuccess) return hip_fail(e, "partial kernel launch");
   if (plan.combine) {

@@ -130,16 +130,66 @@ __device__ __forceinline__ int64_t token_row(const DecodeArgs& a, int b, int t, 
 // Wave64 helpers
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+// Cross-lane exchanges without LDS.  gfx950's row swaps: permlane16_swap
+// of a value with itself returns {x[l], x[l ^ 16]} (in some order) in every
+// lane, permlane32_swap {x[l], x[l ^ 32]}; combining the pair with a
+// commutative op gives the same result in both partner lanes.
+__device__ __forceinline__ float max_xor16(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+
+// DPP lane patterns within a row of 16 lanes: xor 1, xor 2 (quad perms),
+// reverse within 8 (half mirror), reverse within 16 (mirror), rotate by 4
+// and by 8.
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+constexpr int kDppRor4 = 0x124, kDppRor8 = 0x128;
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_amdgcn_update_dpp(0.0f, x, CTRL, 0xF, 0xF, false);
+}
+
+// Sum over the CPR lanes l ^ m (m < CPR; CPR = 4, 8 or 16 consecutive
+// lanes), result in all of them.  Pairs are added in an order that
+// commutativity makes identical in every lane.
+template <int CPR>
+__device__ __forceinline__ float sum_low_lanes(float x) {
+  x += dpp<kDppXor1>(x);
+  x += dpp<kDppXor2>(x);
+  if constexpr (CPR >= 8) x += dpp<kDppHalfMirror>(x);
+  if constexpr (CPR >= 16) x += dpp<kDppMirror>(x);
   return x;
 }
 
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-  return x;
+// Max / sum over the lanes that share l % CPR (the 64 / CPR lanes l + k CPR),
+// result in all of them.
+template <int CPR>
+__device__ __forceinline__ float max_high_lanes(float x) {
+  if constexpr (CPR <= 4) x = fmaxf(x, dpp<kDppRor4>(x));
+  if constexpr (CPR <= 8) x = fmaxf(x, dpp<kDppRor8>(x));
+  return max_xor32(max_xor16(x));
+}
+template <int CPR>
+__device__ __forceinline__ float sum_high_lanes(float x) {
+  if constexpr (CPR <= 4) x += dpp<kDppRor4>(x);
+  if constexpr (CPR <= 8) x += dpp<kDppRor8>(x);
+  return sum_xor32(sum_xor16(x));
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -158,6 +208,11 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 __device__ __forceinline__ void fp8x4_to_bf16x4(uint32_t w, uint32_t& lo, uint32_t& hi) {
   lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
   hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+}
+
+// Two bf16 products plus c, accumulated in fp32 (v_dot2_f32_bf16).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
 }
 
 // D(16x16 fp32) += A(16x32 bf16) * B(32x16 bf16).  Lane l holds A row l%16,

@@ -105,15 +105,29 @@ constexpr int kDense = 0, kIndirect = 1, kPacked = 2;
 // bf16 d = 128, whose two register buffers of whole-row loads alone take
 // 128 VGPRs -- squeezed into half the file it spills, and every spill
 // reload waits for all loads in flight.
-template <int D, bool FP8, int MB>
-constexpr int partial_min_blocks() { return (MB == 1 && (FP8 || D == 64)) ? 2 : 1; }
+// The VALU variant keeps RV x (8 or 16) fp32 accumulators and every score
+// of a tile per lane, and also takes the whole file.
+template <int D, bool FP8, int MB, int RV>
+constexpr int partial_min_blocks() { return (MB == 1 && (FP8 || D == 64) && RV == 0) ? 2 : 1; }
 
-template <int D, bool FP8, int MODE, int MB>
-__global__ void __launch_bounds__(kPThreads, (partial_min_blocks<D, FP8, MB>())) gqa_partial_kernel(DecodeArgs a) {
+// MB: 16-row MFMA blocks (RV = 0).  RV > 0 selects the VALU variant for up
+// to RV query rows (MB = 1): the same loads, LDS staging and pipeline, with
+// the two products done by v_dot2_f32_bf16 and fp32 FMAs instead of MFMA.
+//   QK: lane (token slot l / CPR, chunk c = l % CPR) dots its ELT elements
+//       of K with the same elements of each Q row; a DPP sum over the CPR
+//       lanes of the token completes the score in all of them.
+//   PV: the lane accumulates p x V over its own token slot for its ELT
+//       columns; the token slots are summed once, after the last tile.
+template <int D, bool FP8, int MODE, int MB, int RV>
+__global__ void __launch_bounds__(kPThreads, (partial_min_blocks<D, FP8, MB, RV>())) gqa_partial_kernel(DecodeArgs a) {
   using TS = TileShape<D, FP8>;
   constexpr int RB = TS::RB, CPR = TS::CPR, TPI = TS::TPI, NLD = TS::NLD, KK = TS::KK, NB = TS::NB;
   constexpr bool INDIRECT = MODE == kIndirect;
   constexpr bool PACKED = MODE == kPacked;
+  constexpr bool VALU = RV > 0;
+  constexpr int ELT = FP8 ? 16 : 8;             // elements of one 16-byte chunk
+  constexpr int NR = VALU ? RV : MB;            // running-state rows per lane
+  static_assert(!VALU || MB == 1, "the VALU variant computes one block of at most 16 rows");
   static_assert(kPWaves * 16 * D * 4 <= kPWaves * wave_tile_bytes(D, FP8), "accumulators fit in the tiles");
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -192,10 +206,28 @@ __global__ void __launch_bounds__(kPThreads, (partial_min_blocks<D, FP8, MB>()))
 
   // Q as the B operand of S^T = K Q^T: lane = query row, 8 d per k-step.
   // Row r of the group is (query token i = r / G, head g*G + r % G).
-  u32x4 qop[MB][KK];
-  int lim[MB];
+  // VALU: every lane holds the ELT elements of its chunk for all RV rows.
+  u32x4 qop[VALU ? 1 : MB][KK];
+  uint32_t qv[VALU ? RV : 1][ELT / 2];
+  int lim[NR];
+  if constexpr (VALU) {
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
+    for (int r = 0; r < RV; ++r) {
+      const int rr = min(r, a.rows - 1);
+      const int i = rr / a.group;
+      lim[r] = a.causal ? (n - a.s_q + i) : 0x7fffffff;
+      const int h = g * a.group + (rr - i * a.group);
+      const uint16_t* qrow = a.q + ((int64_t)(b * a.s_q + i) * a.h_q + h) * D + (lane % CPR) * ELT;
+#pragma unroll
+      for (int j = 0; j < ELT / 8; ++j) {
+        const u32x4 v = r < a.rows ? *reinterpret_cast<const u32x4*>(qrow + 8 * j) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) qv[r][4 * j + c] = v[c];
+      }
+    }
+  }
+#pragma unroll
+  for (int mb = 0; mb < (VALU ? 0 : MB); ++mb) {
     const int r = mb * 16 + m16;
     const int rr = min(r, a.rows - 1);
     const int i = rr / a.group;
@@ -215,15 +247,22 @@ __global__ void __launch_bounds__(kPThreads, (partial_min_blocks<D, FP8, MB>()))
   float sc = a.scale_log2;
   if constexpr (FP8) sc *= a.k_scale[b * a.h_kv + g];
 
-  f32x4 acc[MB][NB];
-  float mrun[MB], lrun[MB];
+  f32x4 acc[VALU ? 1 : MB][NB];
+  float accv[VALU ? RV : 1][ELT];
+  float mrun[NR], lrun[NR];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    mrun[mb] = -INFINITY;
-    lrun[mb] = 0.f;
+  for (int r = 0; r < NR; ++r) {
+    mrun[r] = -INFINITY;
+    lrun[r] = 0.f;
+  }
+#pragma unroll
+  for (int mb = 0; mb < (VALU ? 1 : MB); ++mb)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+#pragma unroll
+  for (int r = 0; r < (VALU ? RV : 1); ++r)
+#pragma unroll
+    for (int e = 0; e < ELT; ++e) accv[r][e] = 0.f;
 
   unsigned char* wtiles = tiles + wave * wave_tile_bytes(D, FP8);
   u32x4* kt = reinterpret_cast<u32x4*>(wtiles);
@@ -233,7 +272,10 @@ __global__ void __launch_bounds__(kPThreads, (partial_min_blocks<D, FP8, MB>()))
   const int ltok = lane / CPR;                  // token of this lane within a wave-wide load
   const int lch = lane % CPR;                   // 16-byte chunk of this lane
 
-  auto row_of = [&](int p) -> int64_t {
+  // Every helper lambda below is forced inline: one left out of line is
+  // called with its captures in a stack frame, and every pointer it reads
+  // from there is generic -- flat loads for HBM and LDS alike.
+  auto row_of = [&](int p) __attribute__((always_inline)) -> int64_t {
     if constexpr (INDIRECT) {
       return trow[p - start];
     } else {
@@ -245,7 +287,7 @@ __global__ void __launch_bounds__(kPThreads, (partial_min_blocks<D, FP8, MB>()))
   // load i covering tokens i*TPI .. +TPI-1 of the tile in whole rows.  A
   // non-real tile (the prefetch slot after a wave's last tile) reads one
   // 16-byte location with every lane: no branch, no HBM traffic to speak of.
-  auto load_tile = [&](int tile, u32x4 (&kr)[NLD], u32x4 (&vr)[NLD], bool real) {
+  auto load_tile = [&](int tile, u32x4 (&kr)[NLD], u32x4 (&vr)[NLD], bool real) __attribute__((always_inline)) {
     const int tb = start + tile * kTile;
     const int lane_on = real ? 1 : 0;
 #pragma unroll
@@ -258,7 +300,7 @@ __global__ void __launch_bounds__(kPThreads, (partial_min_blocks<D, FP8, MB>()))
   };
 
   // Stage a tile's K (raw chunks) and V (bf16) in this wave's LDS tiles.
-  auto stage_tile = [&](const u32x4 (&kr)[NLD], const u32x4 (&vr)[NLD]) {
+  auto stage_tile = [&](const u32x4 (&kr)[NLD], const u32x4 (&vr)[NLD]) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
       const int tok = i * TPI + ltok;
@@ -286,7 +328,7 @@ __global__ void __launch_bounds__(kPThreads, (partial_min_blocks<D, FP8, MB>()))
   };
 
   // Compute one staged tile (from LDS only).
-  auto compute_tile = [&](int tile) {
+  auto compute_tile = [&](int tile) __attribute__((always_inline)) {
     const int tb = start + tile * kTile;
 
     // K operands: lane (m16, qd) reads token 16 hb + m16, contraction chunk
@@ -357,8 +399,7 @@ __global__ void __launch_bounds__(kPThreads, (partial_min_blocks<D, FP8, MB>()))
     for (int mb = 0; mb < MB; ++mb) {
       float mx = fmaxf(fmaxf(fmaxf(s[0][mb][0], s[0][mb][1]), fmaxf(s[0][mb][2], s[0][mb][3])),
                        fmaxf(fmaxf(s[1][mb][0], s[1][mb][1]), fmaxf(s[1][mb][2], s[1][mb][3])));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = max_xor32(max_xor16(mx));  // over the four lane groups of the column
       const float mnew = fmaxf(mrun[mb], mx);
       const float muse = (mnew == -INFINITY) ? 0.f : mnew;
       const float alpha = fast_exp2(mrun[mb] - muse);
@@ -409,10 +450,111 @@ __global__ void __launch_bounds__(kPThreads, (partial_min_blocks<D, FP8, MB>()))
     __asm__ __volatile__("" ::: "memory");
   };
 
+  // VALU variant of compute_tile (RV rows).  Lane (ltok, lch) reads, for
+  // each wave-wide row group i, chunk lch of token i*TPI + ltok from the
+  // staged K and V tiles.
+  auto compute_tile_valu = [&](int tile) __attribute__((always_inline)) {
+    const int tb = start + tile * kTile;
+    float sv[NLD][VALU ? RV : 1];
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int tok = i * TPI + ltok;
+      const u32x4 c = kt[tok * CPR + kchunk<CPR>(lch, tok)];
+      uint32_t kp[ELT / 2];
+      if constexpr (FP8) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) fp8x4_to_bf16x4(c[w], kp[2 * w], kp[2 * w + 1]);
+      } else {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) kp[w] = c[w];
+      }
+#pragma unroll
+      for (int r = 0; r < RV; ++r) {
+        float d = 0.f;
+#pragma unroll
+        for (int j = 0; j < ELT / 2; ++j) d = dot2_bf16(kp[j], qv[r][j], d);
+        sv[i][r] = sum_low_lanes<CPR>(d) * sc;
+      }
+    }
+
+    const bool need_mask = INDIRECT || (tb + kTile > end) || (a.causal && tb + kTile - 1 > n - a.s_q);
+    if (need_mask) {
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) {
+        const int p = tb + i * TPI + ltok;
+        int t;
+        bool ok;
+        if constexpr (INDIRECT) {
+          t = ttok[p - start];
+          ok = t >= 0;
+        } else {
+          t = p;
+          ok = p < end;
+        }
+#pragma unroll
+        for (int r = 0; r < RV; ++r)
+          if (!ok || t > lim[r]) sv[i][r] = -INFINITY;
+      }
+    }
+
+    // Online softmax per row: the tile maximum over every token slot; each
+    // lane's sum covers its own slot (slots are summed after the last tile).
+#pragma unroll
+    for (int r = 0; r < RV; ++r) {
+      float mx = sv[0][r];
+#pragma unroll
+      for (int i = 1; i < NLD; ++i) mx = fmaxf(mx, sv[i][r]);
+      mx = max_high_lanes<CPR>(mx);
+      const float mnew = fmaxf(mrun[r], mx);
+      const float muse = (mnew == -INFINITY) ? 0.f : mnew;
+      const float alpha = fast_exp2(mrun[r] - muse);
+      float ps = 0.f;
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) {
+        sv[i][r] = fast_exp2(sv[i][r] - muse);
+        ps += sv[i][r];
+      }
+      lrun[r] = lrun[r] * alpha + ps;
+      mrun[r] = mnew;
+#pragma unroll
+      for (int e = 0; e < ELT; ++e) accv[r][e] *= alpha;
+    }
+
+    // PV: columns [ELT lch, +ELT) of each of the lane's tokens (bf16 in LDS).
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int tok = i * TPI + ltok;
+      float vf[ELT];
+#pragma unroll
+      for (int h = 0; h < ELT / 8; ++h) {
+        const int col = ELT * lch + 8 * h;     // first column of this 8-element half block
+        const u32x4 w = *reinterpret_cast<const u32x4*>(vt + tok * D + 16 * vblk<D>(col >> 4, tok) + (col & 8));
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          vf[8 * h + 2 * c] = bf16_lo(w[c]);
+          vf[8 * h + 2 * c + 1] = bf16_hi(w[c]);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < RV; ++r)
+#pragma unroll
+        for (int e = 0; e < ELT; ++e) accv[r][e] = fmaf(sv[i][r], vf[e], accv[r][e]);
+    }
+    __builtin_amdgcn_wave_barrier();
+    __asm__ __volatile__("" ::: "memory");
+  };
+
+  auto compute = [&](int tile) __attribute__((always_inline)) {
+    if constexpr (VALU)
+      compute_tile_valu(tile);
+    else
+      compute_tile(tile);
+  };
+
   // Keeps every load issued so far above this point: no IR pass may sink a
   // load past a possible memory write, and the machine scheduler may not
   // move instructions across the barrier.
-  auto issue_fence = [] {
+  auto issue_fence = []() __attribute__((always_inline)) {
     __asm__ __volatile__("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -444,7 +586,7 @@ __global__ void __launch_bounds__(kPThreads, (partial_min_blocks<D, FP8, MB>()))
         bool real = ahead < ntiles;
         load_tile(real ? ahead : tile, kA, vA, real);
         issue_fence();
-        compute_tile(tile);
+        compute(tile);
         issue_fence();
         stage_tile(kB, vB);
         issue_fence();
@@ -452,24 +594,31 @@ __global__ void __launch_bounds__(kPThreads, (partial_min_blocks<D, FP8, MB>()))
         real = ahead < ntiles;
         load_tile(real ? ahead : tile, kB, vB, real);
         issue_fence();
-        compute_tile(tile + wph);
+        compute(tile + wph);
         issue_fence();
         tile += 2 * wph;
       }
       if (tile < ntiles) {  // an odd last tile, in A (B holds a dummy)
         stage_tile(kA, vA);
         issue_fence();
-        compute_tile(tile);
+        compute(tile);
         issue_fence();
       }
     }
   }
 
-  // Row sums over the four lane groups.
+  // Row sums over the four lane groups (MFMA) or over the token slots
+  // (VALU, which also sums its accumulators over them).
+  if constexpr (VALU) {
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    lrun[mb] += __shfl_xor(lrun[mb], 16);
-    lrun[mb] += __shfl_xor(lrun[mb], 32);
+    for (int r = 0; r < RV; ++r) {
+      lrun[r] = sum_high_lanes<CPR>(lrun[r]);
+#pragma unroll
+      for (int e = 0; e < ELT; ++e) accv[r][e] = sum_high_lanes<CPR>(accv[r][e]);
+    }
+  } else {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) lrun[mb] = sum_xor32(sum_xor16(lrun[mb]));
   }
 
   // Merge the waves of each head, one 16-row block at a time, and write.
@@ -482,13 +631,31 @@ __global__ void __launch_bounds__(kPThreads, (partial_min_blocks<D, FP8, MB>()))
   for (int mb = 0; mb < MB; ++mb) {
     if (mb * 16 >= a.rows) break;
     __syncthreads();
-    if (qd == 0) {
-      wm[wave * 16 + m16] = mrun[mb];
-      wl[wave * 16 + m16] = lrun[mb];
-    }
+    if constexpr (VALU) {
+      if (lane == 0) {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-      *reinterpret_cast<f32x4*>(wacc + (wave * 16 + m16) * D + 16 * nb + 4 * qd) = acc[mb][nb];
+        for (int r = 0; r < RV; ++r) {
+          wm[wave * 16 + r] = mrun[r];
+          wl[wave * 16 + r] = lrun[r];
+        }
+      }
+      if (ltok == 0) {
+#pragma unroll
+        for (int r = 0; r < RV; ++r)
+#pragma unroll
+          for (int e = 0; e < ELT; e += 4)
+            *reinterpret_cast<f32x4*>(wacc + (wave * 16 + r) * D + ELT * lch + e) =
+                f32x4{accv[r][e], accv[r][e + 1], accv[r][e + 2], accv[r][e + 3]};
+      }
+    } else {
+      if (qd == 0) {
+        wm[wave * 16 + m16] = mrun[mb];
+        wl[wave * 16 + m16] = lrun[mb];
+      }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        *reinterpret_cast<f32x4*>(wacc + (wave * 16 + m16) * D + 16 * nb + 4 * qd) = acc[mb][nb];
+    }
     __syncthreads();
 
     const int nrow = min(16, a.rows - mb * 16);
@@ -690,31 +857,42 @@ __global__ void __launch_bounds__(kThreads) gqa_resolve_kernel(DecodeArgs a, int
 
 // ev0 / ev1 (may be null): events stamped by the dispatch itself at the
 // kernel's start and end, so they time the kernel alone.
-template <int D, bool FP8, int MODE, int MB>
+template <int D, bool FP8, int MODE, int MB, int RV>
 static hipError_t launch_partial_t(const DecodeArgs& a, dim3 grid, hipStream_t st, hipEvent_t ev0,
                                    hipEvent_t ev1) {
   const size_t lds = table_bytes(MODE == kIndirect, a.chunk);
-  hipExtLaunchKernelGGL((gqa_partial_kernel<D, FP8, MODE, MB>), grid, dim3(kPThreads), lds, st, ev0, ev1, 0, a);
+  hipExtLaunchKernelGGL((gqa_partial_kernel<D, FP8, MODE, MB, RV>), grid, dim3(kPThreads), lds, st, ev0, ev1, 0,
+                        a);
   return hipGetLastError();
 }
 
+// rv > 0: the VALU variant for up to rv rows (1, 2, 4 or 8); else mb MFMA
+// blocks.
 template <int D, bool FP8, int MODE>
-static hipError_t launch_mb(const DecodeArgs& a, int mb, dim3 grid, hipStream_t st, hipEvent_t ev0,
+static hipError_t launch_mb(const DecodeArgs& a, int mb, int rv, dim3 grid, hipStream_t st, hipEvent_t ev0,
                             hipEvent_t ev1) {
+  if (rv > 0) {
+    switch (rv) {
+      case 1: return launch_partial_t<D, FP8, MODE, 1, 1>(a, grid, st, ev0, ev1);
+      case 2: return launch_partial_t<D, FP8, MODE, 1, 2>(a, grid, st, ev0, ev1);
+      case 4: return launch_partial_t<D, FP8, MODE, 1, 4>(a, grid, st, ev0, ev1);
+      default: return launch_partial_t<D, FP8, MODE, 1, 8>(a, grid, st, ev0, ev1);
+    }
+  }
   switch (mb) {
-    case 1: return launch_partial_t<D, FP8, MODE, 1>(a, grid, st, ev0, ev1);
-    case 2: return launch_partial_t<D, FP8, MODE, 2>(a, grid, st, ev0, ev1);
-    default: return launch_partial_t<D, FP8, MODE, 4>(a, grid, st, ev0, ev1);
+    case 1: return launch_partial_t<D, FP8, MODE, 1, 0>(a, grid, st, ev0, ev1);
+    case 2: return launch_partial_t<D, FP8, MODE, 2, 0>(a, grid, st, ev0, ev1);
+    default: return launch_partial_t<D, FP8, MODE, 4, 0>(a, grid, st, ev0, ev1);
   }
 }
 
 template <int D, bool FP8>
-static hipError_t launch_mode(const DecodeArgs& a, int mode, int mb, dim3 grid, hipStream_t st, hipEvent_t ev0,
-                              hipEvent_t ev1) {
+static hipError_t launch_mode(const DecodeArgs& a, int mode, int mb, int rv, dim3 grid, hipStream_t st,
+                              hipEvent_t ev0, hipEvent_t ev1) {
   switch (mode) {
-    case kIndirect: return launch_mb<D, FP8, kIndirect>(a, mb, grid, st, ev0, ev1);
-    case kPacked: return launch_mb<D, FP8, kPacked>(a, mb, grid, st, ev0, ev1);
-    default: return launch_mb<D, FP8, kDense>(a, mb, grid, st, ev0, ev1);
+    case kIndirect: return launch_mb<D, FP8, kIndirect>(a, mb, rv, grid, st, ev0, ev1);
+    case kPacked: return launch_mb<D, FP8, kPacked>(a, mb, rv, grid, st, ev0, ev1);
+    default: return launch_mb<D, FP8, kDense>(a, mb, rv, grid, st, ev0, ev1);
   }
 }
 
@@ -723,13 +901,13 @@ size_t partial_lds_bytes(int D, bool fp8, bool indirect, int chunk) {
 }
 
 // mode: 0 dense, 1 indirect (paged / top-K), 2 packed ragged.
-hipError_t launch_partial(const DecodeArgs& a, int D, bool fp8, int mode, int mb, dim3 grid, hipStream_t st,
-                          hipEvent_t ev0, hipEvent_t ev1) {
+hipError_t launch_partial(const DecodeArgs& a, int D, bool fp8, int mode, int mb, int rv, dim3 grid,
+                          hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   if (D == 128)
-    return fp8 ? launch_mode<128, true>(a, mode, mb, grid, st, ev0, ev1)
-               : launch_mode<128, false>(a, mode, mb, grid, st, ev0, ev1);
-  return fp8 ? launch_mode<64, true>(a, mode, mb, grid, st, ev0, ev1)
-             : launch_mode<64, false>(a, mode, mb, grid, st, ev0, ev1);
+    return fp8 ? launch_mode<128, true>(a, mode, mb, rv, grid, st, ev0, ev1)
+               : launch_mode<128, false>(a, mode, mb, rv, grid, st, ev0, ev1);
+  return fp8 ? launch_mode<64, true>(a, mode, mb, rv, grid, st, ev0, ev1)
+             : launch_mode<64, false>(a, mode, mb, rv, grid, st, ev0, ev1);
 }
 
 hipError_t launch_combine(const DecodeArgs& a, int D, dim3 grid, hipStream_t st) {

@@ -74,6 +74,21 @@ enum { GQA_KV_BF16 = 0, GQA_KV_FP8_E4M3FN = 1 };
  * GQA_GATE_HEADWISE:    gate bf16 [B, S_q, H_q],    one value per head.     */
 enum { GQA_GATE_NONE = 0, GQA_GATE_ELEMENTWISE = 1, GQA_GATE_HEADWISE = 2 };
 
+/* Arithmetic of the two products (scores and P.V).  Both run on the same K/V
+ * loads and LDS staging; they differ only in the units that multiply:
+ *   GQA_MATH_MFMA  v_mfma_f32_16x16x32_bf16 on 16-row blocks of query rows
+ *                  (the rows of a KV head's group padded to 16, 32 or 64);
+ *   GQA_MATH_VALU  v_dot2_f32_bf16 and fp32 FMAs on exactly the group's rows,
+ *                  for at most 8 query rows per KV head;
+ *   GQA_MATH_AUTO  the faster one for the row count, as measured on MI355X:
+ *                  VALU for 1 row, MFMA from 2 rows up.
+ * At decode the products are skinny (rows = (H_q / H_kv) * S_q by d); a
+ * tile sized for prefill leaves almost every row of a matrix-unit tile idle
+ * ("When the K/V copy costs more than the attention", "What I was looking
+ * at").  Whether the matrix unit still pays is a question of row count,
+ * settled by measurement.                                                   */
+enum { GQA_MATH_AUTO = 0, GQA_MATH_MFMA = 1, GQA_MATH_VALU = 2 };
+
 typedef struct gqa_decode_params {
   int32_t batch;             /* B >= 0                                                  */
   int32_t s_q;               /* query tokens per request, 1..8                          */
@@ -97,7 +112,7 @@ typedef struct gqa_decode_params {
   int32_t kv_chunk;          /* list positions per split-KV workgroup; 0 = automatic;
                                 else a multiple of 32 (at most 4096 for paged or top-K) */
   int32_t num_cus;           /* compute units to plan for; 0 = ask the current device   */
-  int32_t reserved0;
+  int32_t math;              /* GQA_MATH_*; VALU needs (h_q / h_kv) * s_q <= 8          */
   /* Optional timing hooks: hipEvent_t handles that the split-KV partial
    * kernel's dispatch stamps when the kernel starts and when it ends (so
    * their elapsed time is the kernel alone).  NULL = not used.            */
@@ -107,12 +122,13 @@ typedef struct gqa_decode_params {
 
 typedef struct gqa_decode_plan {
   int32_t rows;              /* query rows sharing one KV head: (h_q / h_kv) * s_q      */
-  int32_t row_blocks;        /* 16-row MFMA blocks the partial kernel computes (1, 2, 4) */
+  int32_t row_blocks;        /* MFMA: 16-row blocks computed (1, 2, 4); VALU: rows
+                                computed (1, 2, 4 or 8, at least the group's rows)      */
   int32_t kv_chunk;          /* list positions per workgroup                            */
   int32_t num_splits;        /* workgroups per (request, KV head) for the longest list  */
   int64_t partial_workgroups;/* grid size of the partial kernel                         */
-  int32_t combine;           /* 1 if the LSE-combine kernel runs (num_splits > 1)       */
-  int32_t reserved0;
+  int32_t combine;           /* 1 if the LSE-combine kernel runs                        */
+  int32_t math;              /* GQA_MATH_MFMA or GQA_MATH_VALU: the path chosen         */
   size_t workspace_bytes;    /* bytes of `workspace` gqa_decode_run needs (0 if none)   */
 } gqa_decode_plan;
 

@@ -43,7 +43,7 @@ def f32(x, device="cuda"):
 class Uploaded:
     """A workload's inputs on the device plus the matching params."""
 
-    def __init__(self, w: gi.Workload, *, kv_chunk=0, gate_mode=None, softmax_scale=None,
+    def __init__(self, w: gi.Workload, *, kv_chunk=0, gate_mode=None, softmax_scale=None, math="auto",
                  device="cuda"):
         s = w.spec
         self.w = w
@@ -80,7 +80,7 @@ class Uploaded:
             batch=B, s_q=Sq, h_q=Hq, h_kv=s.h_kv, head_dim=d, layout=s.layout, kv_dtype=s.kv_dtype,
             causal=s.causal, max_seqlen_kv=w.max_seqlen, seq_capacity=cap, kv_rows=max(kv_rows, 1),
             page_size=s.page_size, max_pages_per_seq=max(mpp, 1) if s.layout == "paged" else 0,
-            topk=s.topk, gate_mode=self.gate_mode, softmax_scale=softmax_scale, kv_chunk=kv_chunk)
+            topk=s.topk, gate_mode=self.gate_mode, softmax_scale=softmax_scale, kv_chunk=kv_chunk, math=math)
         self.plan = G.gqa_decode_make_plan(self.params)
         ws = self.plan["workspace_bytes"]
         self.ws = torch.empty(max(ws, 1), dtype=torch.uint8, device=device)
@@ -137,8 +137,8 @@ def compare(O, LSE, Oref, Lref, *, fp8=False, mask=None, label=""):
     return stats
 
 
-def check_workload(w: gi.Workload, *, kv_chunk=0, gate_mode=None, softmax_scale=None, label=""):
-    up = Uploaded(w, kv_chunk=kv_chunk, gate_mode=gate_mode, softmax_scale=softmax_scale)
+def check_workload(w: gi.Workload, *, kv_chunk=0, gate_mode=None, softmax_scale=None, math="auto", label=""):
+    up = Uploaded(w, kv_chunk=kv_chunk, gate_mode=gate_mode, softmax_scale=softmax_scale, math=math)
     up.run()
     O, LSE = up.result()
     Oref, Lref = oracle(w, gate_mode=up.gate_mode, softmax_scale=softmax_scale)

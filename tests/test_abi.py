@@ -78,6 +78,9 @@ BAD_SHAPES = [
     (dict(kv_chunk=8192, layout="paged", page_size=16, max_pages_per_seq=7, kv_rows=224), 1),
     (dict(softmax_scale=float("inf")), 1),
     (dict(batch=70000), 1),
+    (dict(math=3), 1),
+    (dict(math="valu", h_q=16, h_kv=1), 2),         # 16 rows: more than the VALU path takes
+    (dict(math="valu", h_q=8, h_kv=2, s_q=3), 2),   # 12 rows
 ]
 
 
@@ -97,6 +100,21 @@ def test_plan_never_sizes_an_expansion():
     assert plan["workspace_bytes"] < expansion / 100
     assert plan["workspace_bytes"] == G.gqa_decode_workspace_size(p)
     assert plan["rows"] == 16 and plan["row_blocks"] == 1 and plan["num_splits"] * plan["kv_chunk"] >= 131072
+
+
+def test_plan_math_paths():
+    # VALU computes 4 or 8 rows (at least the group's); MFMA 16-row blocks
+    for rows_kw, rv in ((dict(h_q=8, h_kv=8), 1), (dict(h_q=8, h_kv=4), 2), (dict(h_q=8, h_kv=2), 4),
+                        (dict(h_q=6, h_kv=2), 4), (dict(h_q=8, h_kv=1), 8), (dict(h_q=8, h_kv=4, s_q=3), 8)):
+        plan = G.gqa_decode_make_plan(base(math="valu", **rows_kw))
+        assert plan["math"] == 2 and plan["row_blocks"] == rv
+    plan = G.gqa_decode_make_plan(base(math="mfma", h_q=8, h_kv=1))
+    assert plan["math"] == 1 and plan["row_blocks"] == 1
+    plan = G.gqa_decode_make_plan(base(math="auto", h_q=64, h_kv=2))   # 32 rows: MFMA only
+    assert plan["math"] == 1 and plan["row_blocks"] == 2
+    # the measured crossover: VALU for one row per KV head, MFMA from two
+    assert G.gqa_decode_make_plan(base(math="auto", h_q=8, h_kv=8))["math"] == 2
+    assert G.gqa_decode_make_plan(base(math="auto", h_q=8, h_kv=4))["math"] == 1
 
 
 def test_plan_forced_chunk_and_single_split():

@@ -1,5 +1,6 @@
 """The six named workloads at full size on the GPU, in the planner's default
-launch configuration (the one bench.py times), checked against the fp64
+launch configuration (the one bench.py times) and, where both apply, with the
+other math path, checked against the fp64
 oracle on a seeded sample of output rows computed one by one.  Needs a
 gfx950 GPU; the largest (paged, 4 GiB of K/V) takes about a minute.
 """
@@ -9,6 +10,7 @@ import pytest
 import torch
 
 import gqa_inputs as gi
+import gqa_kv_cache_amd as G
 from gpu_common import Uploaded, compare, log, oracle
 
 pytestmark = pytest.mark.gpu
@@ -29,11 +31,23 @@ def _sample_rows(w, k, seed):
     return sorted(rows)
 
 
-@pytest.mark.parametrize("name", ["tiny", "long128k", "ragged", "ragged_sq8", "paged", "sparse_fp8"])
-def test_named_workload_full_size(name):
-    log(f"[fullsize] {name}: generating")
+# Every workload with the planner's choice; those with at most 8 query rows
+# per KV head also with the other math path.
+FULL_CASES = [(n, "auto") for n in ("tiny", "long128k", "ragged", "ragged_sq8", "paged", "sparse_fp8")] + \
+             [(n, "other") for n in ("tiny", "ragged", "paged", "sparse_fp8")]
+
+
+@pytest.mark.parametrize("name,which", FULL_CASES, ids=[f"{n}-{m}" for n, m in FULL_CASES])
+def test_named_workload_full_size(name, which):
+    log(f"[fullsize] {name} ({which}): generating")
     w = gi.named(name)
-    up = Uploaded(w)
+    math = "auto"
+    if which == "other":
+        s = w.spec
+        shape = G.make_params(batch=1, s_q=s.s_q, h_q=s.h_q, h_kv=s.h_kv, head_dim=s.head_dim, kv_dtype=s.kv_dtype,
+                              max_seqlen_kv=1, seq_capacity=1, kv_rows=1, num_cus=256)
+        math = "valu" if G.gqa_decode_make_plan(shape)["math"] == 1 else "mfma"
+    up = Uploaded(w, math=math)
     log(f"[fullsize] {name}: plan {up.plan}")
     up.run()
     O, LSE = up.result()
