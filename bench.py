@@ -154,6 +154,8 @@ def main():
                     help="math path of the partial kernel (auto: the planner's measured choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold", action="store_true", help="also time single calls after a 1 GiB cache flush")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time K replays of a HIP graph holding one call (launch cost off the host)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run and time a 512 MiB device-to-device copy (counter calibration)")
     args = ap.parse_args()
@@ -271,6 +273,27 @@ def main():
             cold.append(a.elapsed_time(b) * 1e3)
         extra["us_per_call_cold_median"] = round(statistics.median(cold), 3)
         del flush
+    if args.graph:
+        # One call captured into a graph on torch's capture stream (the
+        # binding takes the current stream when none is given), replayed K
+        # times back to back.
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            G.gqa_decode_run(params, q, k, v, seqlens, cu, bt, topk, ks, vs, gate, o, lse, ws, ws.numel(), None)
+        stream.wait_stream(side)
+        with torch.cuda.graph(graph):
+            G.gqa_decode_run(params, q, k, v, seqlens, cu, bt, topk, ks, vs, gate, o, lse, ws, ws.numel(), None)
+        for _ in range(10):
+            graph.replay()
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(K):
+            graph.replay()
+        torch.cuda.synchronize()
+        extra["us_per_call_graph"] = round((time.perf_counter() - t) / K * 1e6, 3)
+        del graph
     if args.calibrate_copy:
         src = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
