@@ -148,7 +148,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="long128k",
-                    choices=["tiny", "long128k", "ragged", "ragged_sq8", "paged", "sparse_fp8"])
+                    choices=["tiny", "long128k", "ragged", "ragged_sq8", "paged", "sparse_fp8",
+                             "long_32x8", "long_8x1", "long_64x8_d64", "long_32x2_d256"])
     ap.add_argument("--kv-chunk", type=int, default=0, help="force list positions per workgroup")
     ap.add_argument("--math", default="auto", choices=["auto", "mfma", "valu"],
                     help="math path of the partial kernel (auto: the planner's measured choice)")

@@ -280,6 +280,17 @@ SPARSE_FP8 = Spec(name="sparse_paged_fp8_gated_b256_32x8_top512", batch=256, h_q
                   page_size=16, pages_per_seq=32, pool_pages=8192, topk=512,
                   topk_mode="permutation", kv_dtype=KV_FP8, gate=True)
 
+# The other shapes of the batch-1, S_q 2, 128K-token results table in "When
+# the K/V copy costs more than the attention" (64/8 d128 is LONG_128K).
+LONG_32X8 = Spec(name="long_32x8_d128_sq2_128k", batch=1, h_q=32, h_kv=8, head_dim=128,
+                 s_q=2, seqlen=131072, causal=True)
+LONG_8X1 = Spec(name="long_8x1_d128_sq2_128k", batch=1, h_q=8, h_kv=1, head_dim=128,
+                s_q=2, seqlen=131072, causal=True)
+LONG_64X8_D64 = Spec(name="long_64x8_d64_sq2_128k", batch=1, h_q=64, h_kv=8, head_dim=64,
+                     s_q=2, seqlen=131072, causal=True)
+LONG_32X2_D256 = Spec(name="long_32x2_d256_sq2_128k", batch=1, h_q=32, h_kv=2, head_dim=256,
+                      s_q=2, seqlen=131072, causal=True)
+
 NAMED = {
     "tiny": (TINY, 1),
     "long128k": (LONG_128K, 2),
@@ -287,6 +298,10 @@ NAMED = {
     "ragged_sq8": (RAGGED_B32_SQ8, 33),
     "paged": (PAGED_B32, 4),
     "sparse_fp8": (SPARSE_FP8, 5),
+    "long_32x8": (LONG_32X8, 6),
+    "long_8x1": (LONG_8X1, 7),
+    "long_64x8_d64": (LONG_64X8_D64, 8),
+    "long_32x2_d256": (LONG_32X2_D256, 9),
 }
 
 

@@ -82,7 +82,8 @@ gqa_status check_shape(const gqa_decode_params* p) {
     return fail(GQA_ERR_INVALID_ARG, "h_q %d / h_kv %d must be positive (h_kv <= 65535)", p->h_q, p->h_kv);
   if (p->h_q % p->h_kv != 0) return fail(GQA_ERR_INVALID_ARG, "h_q %d is not a multiple of h_kv %d", p->h_q, p->h_kv);
   if (p->s_q < 1 || p->s_q > 8) return fail(GQA_ERR_UNSUPPORTED, "s_q %d outside [1, 8]", p->s_q);
-  if (p->head_dim != 64 && p->head_dim != 128) return fail(GQA_ERR_UNSUPPORTED, "head_dim %d is not 64 or 128", p->head_dim);
+  if (p->head_dim != 64 && p->head_dim != 128 && p->head_dim != 256)
+    return fail(GQA_ERR_UNSUPPORTED, "head_dim %d is not 64, 128 or 256", p->head_dim);
   const int64_t rows = (int64_t)(p->h_q / p->h_kv) * p->s_q;
   if (rows > kMaxRows)
     return fail(GQA_ERR_UNSUPPORTED, "(h_q/h_kv)*s_q = %lld query rows per KV head exceeds %d", (long long)rows, kMaxRows);
@@ -124,6 +125,8 @@ gqa_status check_shape(const gqa_decode_params* p) {
   }
   if (p->num_cus < 0) return fail(GQA_ERR_INVALID_ARG, "num_cus %d < 0", p->num_cus);
   if (p->math < GQA_MATH_AUTO || p->math > GQA_MATH_VALU) return fail(GQA_ERR_INVALID_ARG, "unknown math %d", p->math);
+  if (p->math == GQA_MATH_VALU && p->head_dim > 128)
+    return fail(GQA_ERR_UNSUPPORTED, "the VALU path is built for head_dim <= 128");
   if (p->math == GQA_MATH_VALU && rows > kMaxValuRows)
     return fail(GQA_ERR_UNSUPPORTED, "the VALU path takes at most %d query rows per KV head, not %lld", kMaxValuRows,
                 (long long)rows);
@@ -150,7 +153,7 @@ size_t partial_o_bytes(const gqa_decode_params* p, const gqa_decode_plan& plan) 
 // d = 128; three processes each): MFMA is 5-7 % faster from 2 rows up and
 // more than twice as fast at 8, its time flat from 1 to 16 rows; at 1 row
 // the VALU path is as fast or up to 1 % faster.
-int auto_math(int rows) { return rows == 1 ? GQA_MATH_VALU : GQA_MATH_MFMA; }
+int auto_math(int rows, int head_dim) { return rows == 1 && head_dim <= 128 ? GQA_MATH_VALU : GQA_MATH_MFMA; }
 
 gqa_status make_plan(const gqa_decode_params* p, gqa_decode_plan* plan) {
   gqa_status st = check_shape(p);
@@ -158,7 +161,7 @@ gqa_status make_plan(const gqa_decode_params* p, gqa_decode_plan* plan) {
   std::memset(plan, 0, sizeof *plan);
   const int rows = (p->h_q / p->h_kv) * p->s_q;
   plan->rows = rows;
-  plan->math = p->math == GQA_MATH_AUTO ? auto_math(rows) : p->math;
+  plan->math = p->math == GQA_MATH_AUTO ? auto_math(rows, p->head_dim) : p->math;
   if (plan->math == GQA_MATH_VALU)
     plan->row_blocks = rows <= 2 ? rows : (rows <= 4 ? 4 : 8);
   else
@@ -187,6 +190,11 @@ gqa_status make_plan(const gqa_decode_params* p, gqa_decode_plan* plan) {
       chunk = round_up(std::max<int64_t>(per, 128), 128);
       chunk = std::min<int64_t>(chunk, 4096);
       chunk = std::min<int64_t>(chunk, round_up(std::max<int64_t>(L, 1), 32));
+      if (indirect) {
+        // the row table (8 bytes per position) must fit beside the tiles
+        const size_t tiles = gqa::partial_lds_bytes(p->head_dim, p->kv_dtype == GQA_KV_FP8_E4M3FN, false, 0);
+        chunk = std::min<int64_t>(chunk, (int64_t)((kMaxLdsPerWorkgroup - tiles) / 8 / 128 * 128));
+      }
     }
   }
   // Shared memory of one partial workgroup (per-wave K/V tiles plus the

@@ -53,6 +53,11 @@ struct TileShape {
   static constexpr int NLD = kTile / TPI;     // wave-wide loads per tile per tensor
   static constexpr int KK = D / 32;           // MFMA k-steps over d
   static constexpr int NB = D / 16;           // 16-wide d blocks of O
+  // Loads are issued and staged in NPART parts per tile: d = 256 rows are
+  // 512 B, and a whole 32-token tile per register buffer would take 128
+  // VGPRs; in halves it takes 64, like d = 128.
+  static constexpr int NPART = (D == 256) ? 2 : 1;
+  static constexpr int NLDP = NLD / NPART;    // wave-wide loads per part per tensor
 };
 
 // Shared memory of the partial kernel: per wave a K tile (raw 16-byte
@@ -74,10 +79,12 @@ __device__ __forceinline__ int qk_d(int kk, int qd) {
 
 // Physical 16-byte chunk of logical chunk c in the K tile row of token tok:
 // XOR by a token-dependent value so that the 16 rows one A-operand read
-// touches fall on distinct LDS banks.
+// touches fall on distinct LDS banks (rows of 16 or 32 chunks: by the token;
+// of 8 or 4 chunks, where two or four rows share a bank sweep: by the token
+// divided by 2 or 4).
 template <int CPR>
 __device__ __forceinline__ int kchunk(int c, int tok) {
-  return c ^ ((tok >> (CPR == 16 ? 0 : (CPR == 8 ? 1 : 2))) & (CPR - 1));
+  return c ^ ((tok >> (CPR >= 16 ? 0 : (CPR == 8 ? 1 : 2))) & (CPR - 1));
 }
 
 // Physical 16-element block of logical block blk in the V tile row of token
@@ -86,7 +93,7 @@ __device__ __forceinline__ int kchunk(int c, int tok) {
 // share a sweep).
 template <int D>
 __device__ __forceinline__ int vblk(int blk, int tok) {
-  return D == 128 ? (blk ^ (tok & 7)) : (blk ^ ((tok >> 1) & 3));
+  return D >= 128 ? (blk ^ (tok & 7)) : (blk ^ ((tok >> 1) & 3));
 }
 
 // How a partial workgroup finds its work.
@@ -122,6 +129,8 @@ template <int D, bool FP8, int MODE, int MB, int RV>
 __global__ void __launch_bounds__(kPThreads, (partial_min_blocks<D, FP8, MB, RV>())) gqa_partial_kernel(DecodeArgs a) {
   using TS = TileShape<D, FP8>;
   constexpr int RB = TS::RB, CPR = TS::CPR, TPI = TS::TPI, NLD = TS::NLD, KK = TS::KK, NB = TS::NB;
+  constexpr int NPART = TS::NPART, NLDP = TS::NLDP;
+  static_assert(RV == 0 || D <= 128, "the VALU variant is built for d <= 128");
   constexpr bool INDIRECT = MODE == kIndirect;
   constexpr bool PACKED = MODE == kPacked;
   constexpr bool VALU = RV > 0;
@@ -287,38 +296,42 @@ __global__ void __launch_bounds__(kPThreads, (partial_min_blocks<D, FP8, MB, RV>
   // load i covering tokens i*TPI .. +TPI-1 of the tile in whole rows.  A
   // non-real tile (the prefetch slot after a wave's last tile) reads one
   // 16-byte location with every lane: no branch, no HBM traffic to speak of.
-  auto load_tile = [&](int tile, u32x4 (&kr)[NLD], u32x4 (&vr)[NLD], bool real) __attribute__((always_inline)) {
+  auto load_tile = [&](int tile, u32x4 (&kr)[NLDP], u32x4 (&vr)[NLDP], bool real, int part = 0)
+      __attribute__((always_inline)) {
     const int tb = start + tile * kTile;
     const int lane_on = real ? 1 : 0;
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) {
+    for (int ii = 0; ii < NLDP; ++ii) {
+      const int i = part * NLDP + ii;
       const int64_t row = row_of(real ? tb + i * TPI + ltok : start);
       const size_t off = (size_t)row * row_bytes + head_off + (size_t)(16 * lch * lane_on);
-      kr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.k + off));
-      vr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.v + off));
+      kr[ii] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.k + off));
+      vr[ii] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.v + off));
     }
   };
 
   // Stage a tile's K (raw chunks) and V (bf16) in this wave's LDS tiles.
-  auto stage_tile = [&](const u32x4 (&kr)[NLD], const u32x4 (&vr)[NLD]) __attribute__((always_inline)) {
+  auto stage_tile = [&](const u32x4 (&kr)[NLDP], const u32x4 (&vr)[NLDP], int part = 0)
+      __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) {
+    for (int ii = 0; ii < NLDP; ++ii) {
+      const int i = part * NLDP + ii;
       const int tok = i * TPI + ltok;
-      kt[tok * CPR + kchunk<CPR>(lch, tok)] = kr[i];
+      kt[tok * CPR + kchunk<CPR>(lch, tok)] = kr[ii];
       uint16_t* vrow = vt + tok * D;
       if constexpr (FP8) {
         // 16 codes = d [16 lch, +16) = one 16-element block
         uint32_t x0, x1, x2, x3, y0, y1, y2, y3;
-        fp8x4_to_bf16x4(vr[i][0], x0, x1);
-        fp8x4_to_bf16x4(vr[i][1], x2, x3);
-        fp8x4_to_bf16x4(vr[i][2], y0, y1);
-        fp8x4_to_bf16x4(vr[i][3], y2, y3);
+        fp8x4_to_bf16x4(vr[ii][0], x0, x1);
+        fp8x4_to_bf16x4(vr[ii][1], x2, x3);
+        fp8x4_to_bf16x4(vr[ii][2], y0, y1);
+        fp8x4_to_bf16x4(vr[ii][3], y2, y3);
         uint16_t* dst = vrow + 16 * vblk<D>(lch, tok);
         *reinterpret_cast<u32x4*>(dst) = u32x4{x0, x1, x2, x3};
         *reinterpret_cast<u32x4*>(dst + 8) = u32x4{y0, y1, y2, y3};
       } else {
         // 8 elements = d [8 lch, +8) = half of block lch / 2
-        *reinterpret_cast<u32x4*>(vrow + 16 * vblk<D>(lch >> 1, tok) + 8 * (lch & 1)) = vr[i];
+        *reinterpret_cast<u32x4*>(vrow + 16 * vblk<D>(lch >> 1, tok) + 8 * (lch & 1)) = vr[ii];
       }
     }
     // The writes above must land before other lanes read them; a wave's LDS
@@ -331,12 +344,16 @@ __global__ void __launch_bounds__(kPThreads, (partial_min_blocks<D, FP8, MB, RV>
   auto compute_tile = [&](int tile) __attribute__((always_inline)) {
     const int tb = start + tile * kTile;
 
-    // K operands: lane (m16, qd) reads token 16 hb + m16, contraction chunk
-    // of k-step kk; FP8 chunks are unpacked to bf16 in registers.
-    u32x4 kop[2][KK];
+    // S^T for both 16-token halves and every row block.  K operands: lane
+    // (m16, qd) reads token 16 hb + m16, contraction chunk of k-step kk;
+    // FP8 chunks are unpacked to bf16 in registers.  Wide heads (d = 256)
+    // take the halves one after the other, so that only one half's operands
+    // are live (their registers would otherwise spill).
+    f32x4 s[2][MB];
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
       const int tok = hb * 16 + m16;
+      u32x4 kop[KK];
 #pragma unroll
       for (int j = 0; j < (FP8 ? KK / 2 : KK); ++j) {
         const u32x4 c = kt[tok * CPR + kchunk<CPR>(4 * j + qd, tok)];
@@ -346,25 +363,20 @@ __global__ void __launch_bounds__(kPThreads, (partial_min_blocks<D, FP8, MB, RV>
           fp8x4_to_bf16x4(c[1], x2, x3);
           fp8x4_to_bf16x4(c[2], y0, y1);
           fp8x4_to_bf16x4(c[3], y2, y3);
-          kop[hb][2 * j] = u32x4{x0, x1, x2, x3};
-          kop[hb][2 * j + 1] = u32x4{y0, y1, y2, y3};
+          kop[2 * j] = u32x4{x0, x1, x2, x3};
+          kop[2 * j + 1] = u32x4{y0, y1, y2, y3};
         } else {
-          kop[hb][j] = c;
+          kop[j] = c;
         }
       }
-    }
-
-    // S^T for both 16-token halves and every row block.
-    f32x4 s[2][MB];
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) c = mfma_16x16x32(kop[hb][kk], qop[mb][kk], c);
+        for (int kk = 0; kk < KK; ++kk) c = mfma_16x16x32(kop[kk], qop[mb][kk], c);
         s[hb][mb] = c * sc;
       }
+      if constexpr (D == 256) __builtin_amdgcn_sched_barrier(0);
     }
 
     // Masking: slots past the end, masked top-K entries, causal tail.
@@ -570,7 +582,37 @@ __global__ void __launch_bounds__(kPThreads, (partial_min_blocks<D, FP8, MB, RV>
   // what lets the compiler's counter waits keep the younger tile in flight
   // (an exit between the two steps gives the loop a path on which A's
   // loads are the youngest, and every pass then waits for all loads).
-  {
+  if constexpr (NPART == 2) {
+    // d = 256: the two register buffers hold the two halves of a tile.  Each
+    // step stages both halves of the current tile, refilling each buffer at
+    // once with the same half of the next tile, then computes -- so the
+    // next tile (32 KiB of K and V per wave, as two d = 128 tiles) is in
+    // flight while a tile is computed.  One exit test per step.
+    u32x4 kA[NLDP], vA[NLDP], kB[NLDP], vB[NLDP];
+    int tile = sub;
+    if (tile < ntiles) {
+      load_tile(tile, kA, vA, true, 0);
+      issue_fence();
+      load_tile(tile, kB, vB, true, 1);
+      issue_fence();
+      while (true) {
+        const int next = tile + wph;
+        const bool real = next < ntiles;
+        stage_tile(kA, vA, 0);
+        issue_fence();
+        load_tile(real ? next : tile, kA, vA, real, 0);
+        issue_fence();
+        stage_tile(kB, vB, 1);
+        issue_fence();
+        load_tile(real ? next : tile, kB, vB, real, 1);
+        issue_fence();
+        compute(tile);
+        issue_fence();
+        if (!real) break;
+        tile = next;
+      }
+    }
+  } else {
     u32x4 kA[NLD], vA[NLD], kB[NLD], vB[NLD];
     int tile = sub;
     if (tile < ntiles) {
@@ -871,12 +913,14 @@ static hipError_t launch_partial_t(const DecodeArgs& a, dim3 grid, hipStream_t s
 template <int D, bool FP8, int MODE>
 static hipError_t launch_mb(const DecodeArgs& a, int mb, int rv, dim3 grid, hipStream_t st, hipEvent_t ev0,
                             hipEvent_t ev1) {
-  if (rv > 0) {
-    switch (rv) {
-      case 1: return launch_partial_t<D, FP8, MODE, 1, 1>(a, grid, st, ev0, ev1);
-      case 2: return launch_partial_t<D, FP8, MODE, 1, 2>(a, grid, st, ev0, ev1);
-      case 4: return launch_partial_t<D, FP8, MODE, 1, 4>(a, grid, st, ev0, ev1);
-      default: return launch_partial_t<D, FP8, MODE, 1, 8>(a, grid, st, ev0, ev1);
+  if constexpr (D <= 128) {
+    if (rv > 0) {
+      switch (rv) {
+        case 1: return launch_partial_t<D, FP8, MODE, 1, 1>(a, grid, st, ev0, ev1);
+        case 2: return launch_partial_t<D, FP8, MODE, 1, 2>(a, grid, st, ev0, ev1);
+        case 4: return launch_partial_t<D, FP8, MODE, 1, 4>(a, grid, st, ev0, ev1);
+        default: return launch_partial_t<D, FP8, MODE, 1, 8>(a, grid, st, ev0, ev1);
+      }
     }
   }
   switch (mb) {
@@ -903,6 +947,9 @@ size_t partial_lds_bytes(int D, bool fp8, bool indirect, int chunk) {
 // mode: 0 dense, 1 indirect (paged / top-K), 2 packed ragged.
 hipError_t launch_partial(const DecodeArgs& a, int D, bool fp8, int mode, int mb, int rv, dim3 grid,
                           hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+  if (D == 256)
+    return fp8 ? launch_mode<256, true>(a, mode, mb, rv, grid, st, ev0, ev1)
+               : launch_mode<256, false>(a, mode, mb, rv, grid, st, ev0, ev1);
   if (D == 128)
     return fp8 ? launch_mode<128, true>(a, mode, mb, rv, grid, st, ev0, ev1)
                : launch_mode<128, false>(a, mode, mb, rv, grid, st, ev0, ev1);
@@ -911,7 +958,9 @@ hipError_t launch_partial(const DecodeArgs& a, int D, bool fp8, int mode, int mb
 }
 
 hipError_t launch_combine(const DecodeArgs& a, int D, dim3 grid, hipStream_t st) {
-  if (D == 128)
+  if (D == 256)
+    hipLaunchKernelGGL((gqa_combine_kernel<256>), grid, dim3(kThreads), 0, st, a);
+  else if (D == 128)
     hipLaunchKernelGGL((gqa_combine_kernel<128>), grid, dim3(kThreads), 0, st, a);
   else
     hipLaunchKernelGGL((gqa_combine_kernel<64>), grid, dim3(kThreads), 0, st, a);

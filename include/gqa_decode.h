@@ -94,7 +94,7 @@ typedef struct gqa_decode_params {
   int32_t s_q;               /* query tokens per request, 1..8                          */
   int32_t h_q;               /* query heads                                             */
   int32_t h_kv;              /* KV heads; h_q % h_kv == 0, (h_q/h_kv)*s_q <= 64         */
-  int32_t head_dim;          /* 64 or 128                                               */
+  int32_t head_dim;          /* 64, 128 or 256 (the VALU path: 64 or 128)              */
   int32_t layout;            /* GQA_LAYOUT_*                                            */
   int32_t kv_dtype;          /* GQA_KV_*                                                */
   int32_t causal;            /* 1: query i of an S_q block sits at position n_b - S_q + i

@@ -61,6 +61,8 @@ BAD_SHAPES = [
     (dict(s_q=0), 2),
     (dict(s_q=9), 2),
     (dict(head_dim=96), 2),
+    (dict(head_dim=512), 2),
+    (dict(head_dim=256, math="valu"), 2),         # the VALU path is built for d <= 128
     (dict(h_q=128, h_kv=1), 2),             # 128 rows per KV head
     (dict(h_q=16, h_kv=1, s_q=8), 2),       # 128 rows
     (dict(layout=7), 1),
@@ -115,6 +117,17 @@ def test_plan_math_paths():
     # the measured crossover: VALU for one row per KV head, MFMA from two
     assert G.gqa_decode_make_plan(base(math="auto", h_q=8, h_kv=8))["math"] == 2
     assert G.gqa_decode_make_plan(base(math="auto", h_q=8, h_kv=4))["math"] == 1
+
+
+def test_plan_head_dim_256():
+    # MFMA only; an auto plan with one row stays on MFMA for d = 256
+    plan = G.gqa_decode_make_plan(base(head_dim=256, h_q=2, h_kv=2))
+    assert plan["math"] == 1
+    # paged d = 256: the auto chunk keeps the row table beside 128 KiB of tiles
+    p = base(head_dim=256, h_q=32, h_kv=2, layout="paged", page_size=16, max_pages_per_seq=8192,
+             max_seqlen_kv=131072, kv_rows=131072 * 2)
+    plan = G.gqa_decode_make_plan(p)
+    assert plan["kv_chunk"] <= 4032
 
 
 def test_plan_forced_chunk_and_single_split():

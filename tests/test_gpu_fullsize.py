@@ -1,4 +1,4 @@
-"""The six named workloads at full size on the GPU, in the planner's default
+"""The named workloads at full size on the GPU, in the planner's default
 launch configuration (the one bench.py times) and, where both apply, with the
 other math path, checked against the fp64
 oracle on a seeded sample of output rows computed one by one.  Needs a
@@ -33,7 +33,8 @@ def _sample_rows(w, k, seed):
 
 # Every workload with the planner's choice; those with at most 8 query rows
 # per KV head also with the other math path.
-FULL_CASES = [(n, "auto") for n in ("tiny", "long128k", "ragged", "ragged_sq8", "paged", "sparse_fp8")] + \
+FULL_CASES = [(n, "auto") for n in ("tiny", "long128k", "ragged", "ragged_sq8", "paged", "sparse_fp8",
+                                     "long_32x8", "long_8x1", "long_64x8_d64", "long_32x2_d256")] + \
              [(n, "other") for n in ("tiny", "ragged", "paged", "sparse_fp8")]
 
 
