@@ -17,7 +17,7 @@
 #include "gqa_device.h"
 
 namespace gqa {
-hipError_t launch_partial(const DecodeArgs& a, int D, bool fp8, int mode, int mb, int rv, dim3 grid,
+hipError_t launch_partial(const DecodeArgs& a, int D, bool fp8, int mode, int mb, int rv, int share, dim3 grid,
                           hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_combine(const DecodeArgs& a, int D, dim3 grid, hipStream_t st);
 hipError_t launch_resolve(const DecodeArgs& a, int64_t* out, int list_cap, hipStream_t st);
@@ -155,6 +155,23 @@ size_t partial_o_bytes(const gqa_decode_params* p, const gqa_decode_plan& plan) 
 // the VALU path is as fast or up to 1 % faster.
 int auto_math(int rows, int head_dim) { return rows == 1 && head_dim <= 128 ? GQA_MATH_VALU : GQA_MATH_MFMA; }
 
+// Waves per head that split the rows (2) rather than the tiles (1).  Two
+// 16-row MFMA blocks of d = 256 (17 to 32 rows) do not fit one wave's
+// registers; instead each of a head's two waves computes one block over
+// every tile, and the two share the tiles' loads through LDS.  Needs an
+// even H_kv: a workgroup then covers kPWaves / 2 heads.
+int row_share(const gqa_decode_params* p, const gqa_decode_plan& plan) {
+  return p->head_dim == 256 && plan.math == GQA_MATH_MFMA && plan.row_blocks == 2 &&
+                 p->h_kv % (gqa::kPWaves / 2) == 0
+             ? 2
+             : 1;
+}
+
+// KV heads per partial workgroup for this plan.
+int plan_hpw(const gqa_decode_params* p, const gqa_decode_plan& plan) {
+  return row_share(p, plan) == 2 ? gqa::kPWaves / 2 : heads_per_wg(p->h_kv);
+}
+
 gqa_status make_plan(const gqa_decode_params* p, gqa_decode_plan* plan) {
   gqa_status st = check_shape(p);
   if (st != GQA_OK) return st;
@@ -170,7 +187,7 @@ gqa_status make_plan(const gqa_decode_params* p, gqa_decode_plan* plan) {
   const bool packed = packed_mode(p);
   const int64_t L = p->topk > 0 ? p->topk : p->max_seqlen_kv;
   const int64_t pairs = (int64_t)p->batch * p->h_kv;
-  const int hpw = heads_per_wg(p->h_kv);
+  const int hpw = plan_hpw(p, *plan);
   const int64_t groups = p->h_kv / hpw;
   int64_t chunk = p->kv_chunk;
   if (chunk == 0) {
@@ -242,7 +259,7 @@ void fill_args(gqa::DecodeArgs& a, const gqa_decode_params* p, const gqa_decode_
   a.gate_mode = p->gate_mode;
   a.chunk = plan.kv_chunk;
   a.num_splits = plan.num_splits;
-  a.heads_per_wg = heads_per_wg(p->h_kv);
+  a.heads_per_wg = plan_hpw(p, plan);
   a.packed = packed_mode(p) ? 1 : 0;
   if (a.packed) {
     a.part_sb = (int64_t)p->h_kv * plan.rows;
@@ -350,10 +367,10 @@ gqa_status gqa_decode_run(const gqa_decode_params* p, const void* q, const void*
   const bool indirect = p->layout == GQA_LAYOUT_PAGED || p->topk > 0;
   const int mode = a.packed ? 2 : (indirect ? 1 : 0);
   // Packed chunks span requests: one grid row covers the whole batch.
-  const dim3 grid(plan.num_splits, p->h_kv / heads_per_wg(p->h_kv), a.packed ? 1 : p->batch);
+  const dim3 grid(plan.num_splits, p->h_kv / a.heads_per_wg, a.packed ? 1 : p->batch);
   const bool valu = plan.math == GQA_MATH_VALU;
   hipError_t e = gqa::launch_partial(a, p->head_dim, p->kv_dtype == GQA_KV_FP8_E4M3FN, mode, valu ? 1 : plan.row_blocks,
-                                     valu ? plan.row_blocks : 0, grid, s,
+                                     valu ? plan.row_blocks : 0, row_share(p, plan), grid, s,
                                      static_cast<hipEvent_t>(p->partial_event_begin),
                                      static_cast<hipEvent_t>(p->partial_event_end));
   if (e != hipSuccess) return hip_fail(e, "partial kernel launch");

@@ -155,6 +155,15 @@ __device__ __forceinline__ float sum_xor32(float x) {
   return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
 }
 
+// Workgroup barrier that orders LDS only: the release/acquire fences are
+// scoped to local memory, so the waves' HBM loads in flight stay in flight
+// (a full __syncthreads waits for them too).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // DPP lane patterns within a row of 16 lanes: xor 1, xor 2 (quad perms),
 // reverse within 8 (half mirror), reverse within 16 (mirror), rotate by 4
 // and by 8.

@@ -114,8 +114,8 @@ constexpr int kDense = 0, kIndirect = 1, kPacked = 2;
 // reload waits for all loads in flight.
 // The VALU variant keeps RV x (8 or 16) fp32 accumulators and every score
 // of a tile per lane, and also takes the whole file.
-template <int D, bool FP8, int MB, int RV>
-constexpr int partial_min_blocks() { return (MB == 1 && (FP8 || D == 64) && RV == 0) ? 2 : 1; }
+template <int D, bool FP8, int MB, int RV, int SHARE>
+constexpr int partial_min_blocks() { return (MB == 1 && (FP8 || D == 64) && RV == 0 && SHARE == 1) ? 2 : 1; }
 
 // MB: 16-row MFMA blocks (RV = 0).  RV > 0 selects the VALU variant for up
 // to RV query rows (MB = 1): the same loads, LDS staging and pipeline, with
@@ -125,12 +125,21 @@ constexpr int partial_min_blocks() { return (MB == 1 && (FP8 || D == 64) && RV =
 //       lanes of the token completes the score in all of them.
 //   PV: the lane accumulates p x V over its own token slot for its ELT
 //       columns; the token slots are summed once, after the last tile.
-template <int D, bool FP8, int MODE, int MB, int RV>
-__global__ void __launch_bounds__(kPThreads, (partial_min_blocks<D, FP8, MB, RV>())) gqa_partial_kernel(DecodeArgs a) {
+// SHARE = 2 (d = 256, 17 to 32 query rows): the two waves of a head split
+// the rows instead of the tiles.  Each computes one 16-row block over every
+// tile of the chunk, and each loads and stages half of every tile into a
+// head-wide, double-buffered LDS tile (an LDS-only barrier per tile).  HBM
+// still reads each tile once, and a wave's registers are those of the
+// one-block kernel: two row blocks of d = 256 in one wave do not fit.
+template <int D, bool FP8, int MODE, int MB, int RV, int SHARE>
+__global__ void __launch_bounds__(kPThreads, (partial_min_blocks<D, FP8, MB, RV, SHARE>()))
+    gqa_partial_kernel(DecodeArgs a) {
   using TS = TileShape<D, FP8>;
   constexpr int RB = TS::RB, CPR = TS::CPR, TPI = TS::TPI, NLD = TS::NLD, KK = TS::KK, NB = TS::NB;
   constexpr int NPART = TS::NPART, NLDP = TS::NLDP;
   static_assert(RV == 0 || D <= 128, "the VALU variant is built for d <= 128");
+  static_assert(SHARE == 1 || (SHARE == 2 && D == 256 && MB == 1 && RV == 0), "row sharing: d = 256, one block per wave");
+  constexpr bool SHARED = SHARE > 1;
   constexpr bool INDIRECT = MODE == kIndirect;
   constexpr bool PACKED = MODE == kPacked;
   constexpr bool VALU = RV > 0;
@@ -152,7 +161,8 @@ __global__ void __launch_bounds__(kPThreads, (partial_min_blocks<D, FP8, MB, RV>
   const int hpw = a.heads_per_wg;
   const int wph = kPWaves / hpw;                 // waves per head
   const int hs = wave % hpw;                    // head slot of this wave
-  const int sub = wave / hpw;                   // this wave's share of the head's tiles
+  const int sub = wave / hpw;                   // this wave's share of the head's tiles (or rows)
+  const int rbase = SHARED ? 16 * sub : 0;      // first query row of this wave's blocks
   const int g0 = blockIdx.y * hpw;
   const int g = g0 + hs;
   const int split = blockIdx.x;
@@ -237,7 +247,7 @@ __global__ void __launch_bounds__(kPThreads, (partial_min_blocks<D, FP8, MB, RV>
   }
 #pragma unroll
   for (int mb = 0; mb < (VALU ? 0 : MB); ++mb) {
-    const int r = mb * 16 + m16;
+    const int r = rbase + mb * 16 + m16;
     const int rr = min(r, a.rows - 1);
     const int i = rr / a.group;
     lim[mb] = a.causal ? (n - a.s_q + i) : 0x7fffffff;
@@ -273,9 +283,16 @@ __global__ void __launch_bounds__(kPThreads, (partial_min_blocks<D, FP8, MB, RV>
 #pragma unroll
     for (int e = 0; e < ELT; ++e) accv[r][e] = 0.f;
 
-  unsigned char* wtiles = tiles + wave * wave_tile_bytes(D, FP8);
+  // Staged K and V tiles: one per wave, or (rows shared) two per head,
+  // alternating by tile parity.
+  unsigned char* wtiles = tiles + (SHARED ? 2 * hs : wave) * wave_tile_bytes(D, FP8);
   u32x4* kt = reinterpret_cast<u32x4*>(wtiles);
   uint16_t* vt = reinterpret_cast<uint16_t*>(wtiles + ktile_chunks(D, FP8) * 16);
+  auto use_buffer = [&](int parity) __attribute__((always_inline)) {
+    unsigned char* t = tiles + (2 * hs + parity) * wave_tile_bytes(D, FP8);
+    kt = reinterpret_cast<u32x4*>(t);
+    vt = reinterpret_cast<uint16_t*>(t + ktile_chunks(D, FP8) * 16);
+  };
   const size_t head_off = (size_t)g * RB;
   const size_t row_bytes = (size_t)a.h_kv * RB;
   const int ltok = lane / CPR;                  // token of this lane within a wave-wide load
@@ -582,7 +599,59 @@ __global__ void __launch_bounds__(kPThreads, (partial_min_blocks<D, FP8, MB, RV>
   // what lets the compiler's counter waits keep the younger tile in flight
   // (an exit between the two steps gives the loop a path on which A's
   // loads are the youngest, and every pass then waits for all loads).
-  if constexpr (NPART == 2) {
+  if constexpr (SHARED) {
+    // Rows shared by the two waves of a head: both walk every tile of the
+    // chunk; wave `sub` loads and stages half `sub` of each tile into the
+    // head's LDS buffer of the tile's parity.  A step stages the next tile's
+    // half into the buffer the previous tile used, refills the staged
+    // registers with the tile two beyond it, and computes the current tile;
+    // the LDS-only barrier that ends the step makes the staged halves
+    // visible and frees the computed buffer, while both register buffers
+    // stay in flight.  Two tiles per pass, one exit test, and a tail for an
+    // odd last tile.
+    u32x4 kA[NLDP], vA[NLDP], kB[NLDP], vB[NLDP];
+    if (ntiles > 0) {
+      load_tile(0, kA, vA, true, sub);
+      issue_fence();
+      load_tile(1 < ntiles ? 1 : 0, kB, vB, 1 < ntiles, sub);
+      issue_fence();
+      use_buffer(0);
+      stage_tile(kA, vA, sub);
+      issue_fence();
+      load_tile(2 < ntiles ? 2 : 0, kA, vA, 2 < ntiles, sub);
+      issue_fence();
+      lds_barrier();
+      int tile = 0;
+      // B holds tile + 1, A holds tile + 2 (dummies past the end); the
+      // buffer of tile's parity holds tile.
+      while (tile + 1 < ntiles) {
+        use_buffer((tile + 1) & 1);
+        stage_tile(kB, vB, sub);
+        issue_fence();
+        load_tile(tile + 3 < ntiles ? tile + 3 : 0, kB, vB, tile + 3 < ntiles, sub);
+        issue_fence();
+        use_buffer(tile & 1);
+        compute(tile);
+        issue_fence();
+        lds_barrier();
+        use_buffer(tile & 1);                       // tile + 2 has tile's parity
+        stage_tile(kA, vA, sub);
+        issue_fence();
+        load_tile(tile + 4 < ntiles ? tile + 4 : 0, kA, vA, tile + 4 < ntiles, sub);
+        issue_fence();
+        use_buffer((tile + 1) & 1);
+        compute(tile + 1);
+        issue_fence();
+        lds_barrier();
+        tile += 2;
+      }
+      if (tile < ntiles) {
+        use_buffer(tile & 1);
+        compute(tile);
+        issue_fence();
+      }
+    }
+  } else if constexpr (NPART == 2) {
     // d = 256: the two register buffers hold the two halves of a tile.  Each
     // step stages both halves of the current tile, refilling each buffer at
     // once with the same half of the next tile, then computes -- so the
@@ -663,104 +732,151 @@ __global__ void __launch_bounds__(kPThreads, (partial_min_blocks<D, FP8, MB, RV>
     for (int mb = 0; mb < MB; ++mb) lrun[mb] = sum_xor32(sum_xor16(lrun[mb]));
   }
 
-  // Merge the waves of each head, one 16-row block at a time, and write.
-  float* wacc = reinterpret_cast<float*>(tiles);
-  float* wm = wstat;
-  float* wl = wstat + kPWaves * 16;
-  const bool final_out = fin;
-  constexpr int D8 = D / 8;
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    if (mb * 16 >= a.rows) break;
-    __syncthreads();
-    if constexpr (VALU) {
-      if (lane == 0) {
-#pragma unroll
-        for (int r = 0; r < RV; ++r) {
-          wm[wave * 16 + r] = mrun[r];
-          wl[wave * 16 + r] = lrun[r];
-        }
-      }
-      if (ltok == 0) {
-#pragma unroll
-        for (int r = 0; r < RV; ++r)
-#pragma unroll
-          for (int e = 0; e < ELT; e += 4)
-            *reinterpret_cast<f32x4*>(wacc + (wave * 16 + r) * D + ELT * lch + e) =
-                f32x4{accv[r][e], accv[r][e + 1], accv[r][e + 2], accv[r][e + 3]};
-      }
-    } else {
-      if (qd == 0) {
-        wm[wave * 16 + m16] = mrun[mb];
-        wl[wave * 16 + m16] = lrun[mb];
-      }
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-        *reinterpret_cast<f32x4*>(wacc + (wave * 16 + m16) * D + 16 * nb + 4 * qd) = acc[mb][nb];
-    }
-    __syncthreads();
-
-    const int nrow = min(16, a.rows - mb * 16);
-    for (int it = threadIdx.x; it < hpw * nrow * D8; it += kPThreads) {
-      const int hh = it / (nrow * D8);
-      const int rem = it - hh * (nrow * D8);
-      const int rl = rem / D8;
-      const int d8 = rem - rl * D8;
-      const int r = mb * 16 + rl;
-      const int gg = g0 + hh;
-      float M = -INFINITY;
-      for (int k = 0; k < wph; ++k) M = fmaxf(M, wm[(hh + k * hpw) * 16 + rl]);
-      float o[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = 0.f;
-      float lse2 = -INFINITY;
-      if (M != -INFINITY) {
-        float sum = 0.f;
-        for (int k = 0; k < wph; ++k) {
-          const int w = hh + k * hpw;
-          const float e = fast_exp2(wm[w * 16 + rl] - M);
-          sum += e * wl[w * 16 + rl];
-          const float* src = wacc + (w * 16 + rl) * D + d8 * 8;
-          const f32x4 x0 = *reinterpret_cast<const f32x4*>(src);
-          const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + 4);
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            o[c] += e * x0[c];
-            o[4 + c] += e * x1[c];
-          }
-        }
-        const float inv = (FP8 ? a.v_scale[b * a.h_kv + gg] : 1.f) / sum;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] *= inv;
-        lse2 = M + __log2f(sum);
-      }
+  if constexpr (SHARED) {
+    // Each wave holds complete rows (16 of its head's group): normalise and
+    // write them from registers.  Lane (m16, qd) has row rbase + m16,
+    // columns 16 nb + 4 qd .. +3.
+    const int r = rbase + m16;
+    if (r < a.rows) {
+      const float m = mrun[0], l = lrun[0];
+      const bool empty = (m == -INFINITY);
+      const float inv = empty ? 0.f : (FP8 ? a.v_scale[b * a.h_kv + g] : 1.f) / l;
+      const float lse2 = empty ? -INFINITY : m + __log2f(l);
       const int i = r / a.group;
-      const int h = gg * a.group + (r - i * a.group);
-      if (final_out) {
-        const int64_t oidx = ((int64_t)(b * a.s_q + i) * a.h_q + h) * D + d8 * 8;
-        if (a.gate_mode == kGateElementwise) {
-          const u32x4 gw = *reinterpret_cast<const u32x4*>(a.gate + oidx);
+      const int h = g * a.group + (r - i * a.group);
+      if (fin) {
+        const int64_t obase = ((int64_t)(b * a.s_q + i) * a.h_q + h) * D;
+        const float sgh =
+            a.gate_mode == kGateHeadwise ? sigmoidf_(bf16_lo(a.gate[(int64_t)(b * a.s_q + i) * a.h_q + h])) : 1.f;
+        // Elementwise gates: every load issued before the first is used.
+        uint2 gw[NB];
+        const bool egate = a.gate_mode == kGateElementwise;
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            o[2 * c] *= sigmoidf_(bf16_lo(gw[c]));
-            o[2 * c + 1] *= sigmoidf_(bf16_hi(gw[c]));
+        for (int nb = 0; nb < NB; ++nb)
+          gw[nb] = egate ? *reinterpret_cast<const uint2*>(a.gate + obase + 16 * nb + 4 * qd) : uint2{0u, 0u};
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const int col = 16 * nb + 4 * qd;
+          float o[4];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) o[c] = acc[0][nb][c] * inv * sgh;
+          if (egate) {
+            o[0] *= sigmoidf_(bf16_lo(gw[nb].x));
+            o[1] *= sigmoidf_(bf16_hi(gw[nb].x));
+            o[2] *= sigmoidf_(bf16_lo(gw[nb].y));
+            o[3] *= sigmoidf_(bf16_hi(gw[nb].y));
           }
-        } else if (a.gate_mode == kGateHeadwise) {
-          const uint32_t gb = a.gate[(int64_t)(b * a.s_q + i) * a.h_q + h];
-          const float sg = sigmoidf_(bf16_lo(gb));
-#pragma unroll
-          for (int e = 0; e < 8; ++e) o[e] *= sg;
+          *reinterpret_cast<uint2*>(a.o + obase + col) = uint2{pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3])};
         }
-        const u32x4 ov = {pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3]), pack_bf16(o[4], o[5]),
-                          pack_bf16(o[6], o[7])};
-        *reinterpret_cast<u32x4*>(a.o + oidx) = ov;
-        if (d8 == 0) a.lse[((int64_t)b * a.h_q + h) * a.s_q + i] = lse2 * 0.69314718055994530942f;
+        if (qd == 0) a.lse[((int64_t)b * a.h_q + h) * a.s_q + i] = lse2 * 0.69314718055994530942f;
       } else {
-        const int64_t prow = b * a.part_sb + gg * a.part_sg + split * a.part_ss + r;
-        float* dst = a.o_part + prow * D + d8 * 8;
-        *reinterpret_cast<f32x4*>(dst) = f32x4{o[0], o[1], o[2], o[3]};
-        *reinterpret_cast<f32x4*>(dst + 4) = f32x4{o[4], o[5], o[6], o[7]};
-        if (d8 == 0) a.lse_part[prow] = lse2;
+        const int64_t prow = b * a.part_sb + g * a.part_sg + split * a.part_ss + r;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          *reinterpret_cast<f32x4*>(a.o_part + prow * D + 16 * nb + 4 * qd) = acc[0][nb] * inv;
+        if (qd == 0) a.lse_part[prow] = lse2;
+      }
+    }
+  } else {
+    // Merge the waves of each head, one 16-row block at a time, and write.
+    float* wacc = reinterpret_cast<float*>(tiles);
+    float* wm = wstat;
+    float* wl = wstat + kPWaves * 16;
+    const bool final_out = fin;
+    constexpr int D8 = D / 8;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      if (mb * 16 >= a.rows) break;
+      __syncthreads();
+      if constexpr (VALU) {
+        if (lane == 0) {
+#pragma unroll
+          for (int r = 0; r < RV; ++r) {
+            wm[wave * 16 + r] = mrun[r];
+            wl[wave * 16 + r] = lrun[r];
+          }
+        }
+        if (ltok == 0) {
+#pragma unroll
+          for (int r = 0; r < RV; ++r)
+#pragma unroll
+            for (int e = 0; e < ELT; e += 4)
+              *reinterpret_cast<f32x4*>(wacc + (wave * 16 + r) * D + ELT * lch + e) =
+                  f32x4{accv[r][e], accv[r][e + 1], accv[r][e + 2], accv[r][e + 3]};
+        }
+      } else {
+        if (qd == 0) {
+          wm[wave * 16 + m16] = mrun[mb];
+          wl[wave * 16 + m16] = lrun[mb];
+        }
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          *reinterpret_cast<f32x4*>(wacc + (wave * 16 + m16) * D + 16 * nb + 4 * qd) = acc[mb][nb];
+      }
+      __syncthreads();
+
+      const int nrow = min(16, a.rows - mb * 16);
+      for (int it = threadIdx.x; it < hpw * nrow * D8; it += kPThreads) {
+        const int hh = it / (nrow * D8);
+        const int rem = it - hh * (nrow * D8);
+        const int rl = rem / D8;
+        const int d8 = rem - rl * D8;
+        const int r = mb * 16 + rl;
+        const int gg = g0 + hh;
+        float M = -INFINITY;
+        for (int k = 0; k < wph; ++k) M = fmaxf(M, wm[(hh + k * hpw) * 16 + rl]);
+        float o[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = 0.f;
+        float lse2 = -INFINITY;
+        if (M != -INFINITY) {
+          float sum = 0.f;
+          for (int k = 0; k < wph; ++k) {
+            const int w = hh + k * hpw;
+            const float e = fast_exp2(wm[w * 16 + rl] - M);
+            sum += e * wl[w * 16 + rl];
+            const float* src = wacc + (w * 16 + rl) * D + d8 * 8;
+            const f32x4 x0 = *reinterpret_cast<const f32x4*>(src);
+            const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + 4);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              o[c] += e * x0[c];
+              o[4 + c] += e * x1[c];
+            }
+          }
+          const float inv = (FP8 ? a.v_scale[b * a.h_kv + gg] : 1.f) / sum;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[e] *= inv;
+          lse2 = M + __log2f(sum);
+        }
+        const int i = r / a.group;
+        const int h = gg * a.group + (r - i * a.group);
+        if (final_out) {
+          const int64_t oidx = ((int64_t)(b * a.s_q + i) * a.h_q + h) * D + d8 * 8;
+          if (a.gate_mode == kGateElementwise) {
+            const u32x4 gw = *reinterpret_cast<const u32x4*>(a.gate + oidx);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              o[2 * c] *= sigmoidf_(bf16_lo(gw[c]));
+              o[2 * c + 1] *= sigmoidf_(bf16_hi(gw[c]));
+            }
+          } else if (a.gate_mode == kGateHeadwise) {
+            const uint32_t gb = a.gate[(int64_t)(b * a.s_q + i) * a.h_q + h];
+            const float sg = sigmoidf_(bf16_lo(gb));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] *= sg;
+          }
+          const u32x4 ov = {pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3]), pack_bf16(o[4], o[5]),
+                            pack_bf16(o[6], o[7])};
+          *reinterpret_cast<u32x4*>(a.o + oidx) = ov;
+          if (d8 == 0) a.lse[((int64_t)b * a.h_q + h) * a.s_q + i] = lse2 * 0.69314718055994530942f;
+        } else {
+          const int64_t prow = b * a.part_sb + gg * a.part_sg + split * a.part_ss + r;
+          float* dst = a.o_part + prow * D + d8 * 8;
+          *reinterpret_cast<f32x4*>(dst) = f32x4{o[0], o[1], o[2], o[3]};
+          *reinterpret_cast<f32x4*>(dst + 4) = f32x4{o[4], o[5], o[6], o[7]};
+          if (d8 == 0) a.lse_part[prow] = lse2;
+        }
       }
     }
   }
@@ -899,20 +1015,23 @@ __global__ void __launch_bounds__(kThreads) gqa_resolve_kernel(DecodeArgs a, int
 
 // ev0 / ev1 (may be null): events stamped by the dispatch itself at the
 // kernel's start and end, so they time the kernel alone.
-template <int D, bool FP8, int MODE, int MB, int RV>
+template <int D, bool FP8, int MODE, int MB, int RV, int SHARE = 1>
 static hipError_t launch_partial_t(const DecodeArgs& a, dim3 grid, hipStream_t st, hipEvent_t ev0,
                                    hipEvent_t ev1) {
   const size_t lds = table_bytes(MODE == kIndirect, a.chunk);
-  hipExtLaunchKernelGGL((gqa_partial_kernel<D, FP8, MODE, MB, RV>), grid, dim3(kPThreads), lds, st, ev0, ev1, 0,
+  hipExtLaunchKernelGGL((gqa_partial_kernel<D, FP8, MODE, MB, RV, SHARE>), grid, dim3(kPThreads), lds, st, ev0, ev1, 0,
                         a);
   return hipGetLastError();
 }
 
-// rv > 0: the VALU variant for up to rv rows (1, 2, 4 or 8); else mb MFMA
-// blocks.
+// rv > 0: the VALU variant for up to rv rows (1, 2, 4 or 8); share = 2:
+// two waves per head, one 16-row block each (d = 256); else mb MFMA blocks.
 template <int D, bool FP8, int MODE>
-static hipError_t launch_mb(const DecodeArgs& a, int mb, int rv, dim3 grid, hipStream_t st, hipEvent_t ev0,
-                            hipEvent_t ev1) {
+static hipError_t launch_mb(const DecodeArgs& a, int mb, int rv, int share, dim3 grid, hipStream_t st,
+                            hipEvent_t ev0, hipEvent_t ev1) {
+  if constexpr (D == 256) {
+    if (share == 2) return launch_partial_t<D, FP8, MODE, 1, 0, 2>(a, grid, st, ev0, ev1);
+  }
   if constexpr (D <= 128) {
     if (rv > 0) {
       switch (rv) {
@@ -931,12 +1050,12 @@ static hipError_t launch_mb(const DecodeArgs& a, int mb, int rv, dim3 grid, hipS
 }
 
 template <int D, bool FP8>
-static hipError_t launch_mode(const DecodeArgs& a, int mode, int mb, int rv, dim3 grid, hipStream_t st,
-                              hipEvent_t ev0, hipEvent_t ev1) {
+static hipError_t launch_mode(const DecodeArgs& a, int mode, int mb, int rv, int share, dim3 grid,
+                              hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   switch (mode) {
-    case kIndirect: return launch_mb<D, FP8, kIndirect>(a, mb, rv, grid, st, ev0, ev1);
-    case kPacked: return launch_mb<D, FP8, kPacked>(a, mb, rv, grid, st, ev0, ev1);
-    default: return launch_mb<D, FP8, kDense>(a, mb, rv, grid, st, ev0, ev1);
+    case kIndirect: return launch_mb<D, FP8, kIndirect>(a, mb, rv, share, grid, st, ev0, ev1);
+    case kPacked: return launch_mb<D, FP8, kPacked>(a, mb, rv, share, grid, st, ev0, ev1);
+    default: return launch_mb<D, FP8, kDense>(a, mb, rv, share, grid, st, ev0, ev1);
   }
 }
 
@@ -945,16 +1064,16 @@ size_t partial_lds_bytes(int D, bool fp8, bool indirect, int chunk) {
 }
 
 // mode: 0 dense, 1 indirect (paged / top-K), 2 packed ragged.
-hipError_t launch_partial(const DecodeArgs& a, int D, bool fp8, int mode, int mb, int rv, dim3 grid,
+hipError_t launch_partial(const DecodeArgs& a, int D, bool fp8, int mode, int mb, int rv, int share, dim3 grid,
                           hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   if (D == 256)
-    return fp8 ? launch_mode<256, true>(a, mode, mb, rv, grid, st, ev0, ev1)
-               : launch_mode<256, false>(a, mode, mb, rv, grid, st, ev0, ev1);
+    return fp8 ? launch_mode<256, true>(a, mode, mb, rv, share, grid, st, ev0, ev1)
+               : launch_mode<256, false>(a, mode, mb, rv, share, grid, st, ev0, ev1);
   if (D == 128)
-    return fp8 ? launch_mode<128, true>(a, mode, mb, rv, grid, st, ev0, ev1)
-               : launch_mode<128, false>(a, mode, mb, rv, grid, st, ev0, ev1);
-  return fp8 ? launch_mode<64, true>(a, mode, mb, rv, grid, st, ev0, ev1)
-             : launch_mode<64, false>(a, mode, mb, rv, grid, st, ev0, ev1);
+    return fp8 ? launch_mode<128, true>(a, mode, mb, rv, share, grid, st, ev0, ev1)
+               : launch_mode<128, false>(a, mode, mb, rv, share, grid, st, ev0, ev1);
+  return fp8 ? launch_mode<64, true>(a, mode, mb, rv, share, grid, st, ev0, ev1)
+             : launch_mode<64, false>(a, mode, mb, rv, share, grid, st, ev0, ev1);
 }
 
 hipError_t launch_combine(const DecodeArgs& a, int D, dim3 grid, hipStream_t st) {

@@ -100,3 +100,33 @@ def test_d256_one_hot_rows(chunk):
         for h in range(g * 4, g * 4 + 4):
             assert np.array_equal(O[b, 0, h], vf[row, g]), f"(b={b}, h={h}) expected row {row}"
     log(f"  d256 one-hot chunk={chunk}: exact")
+
+
+# 17 to 32 rows with an even H_kv: the two waves of a head take one 16-row
+# block each and share every tile through LDS.  Odd H_kv keeps two blocks
+# in one wave.
+@pytest.mark.parametrize("hq,hkv,sq", [(24, 1, 1), (48, 2, 1), (16, 2, 3), (20, 4, 4), (34, 2, 1), (32, 1, 1),
+                                       (96, 3, 1)])
+def test_d256_shared_rows_dense(hq, hkv, sq):
+    s = spec(h_q=hq, h_kv=hkv, s_q=sq, causal=sq > 1, fixed_lengths=(1500, 33, 1))
+    check_workload(gi.build(s, seed=800 + hq + hkv + sq), label=f"d256 shared {hq}/{hkv} S_q={sq}")
+
+
+@pytest.mark.parametrize("layout,chunk", [("ragged", 0), ("ragged", 64), ("paged", 0), ("paged", 32),
+                                          ("contiguous", 32)])
+def test_d256_shared_rows_layouts(layout, chunk):
+    s = spec(layout=layout, h_q=48, h_kv=2, s_q=1, page_size=16, fixed_lengths=(5, 0, 400, 97))
+    check_workload(gi.build(s, seed=900 + chunk), kv_chunk=chunk, label=f"d256 shared {layout} chunk {chunk}")
+
+
+@pytest.mark.parametrize("gate_mode,mode", [("elementwise", "permutation"), ("headwise", "random_masked")])
+def test_d256_shared_rows_fp8_sparse_gated(gate_mode, mode):
+    lengths = (256, 256) if mode == "permutation" else (256, 100)
+    s = spec(layout="paged", h_q=24, h_kv=2, s_q=2, causal=True, page_size=16, topk=256, topk_mode=mode,
+             kv_dtype=gi.KV_FP8, gate=True, fixed_lengths=lengths)
+    check_workload(gi.build(s, seed=1000), gate_mode=gate_mode, label=f"d256 shared fp8 sparse {gate_mode}")
+
+
+def test_d256_shared_rows_headwise_gate_bf16():
+    s = spec(h_q=64, h_kv=2, s_q=1, gate=True, fixed_lengths=(777, 64))
+    check_workload(gi.build(s, seed=1100), gate_mode="headwise", label="d256 shared bf16 headwise gate")
