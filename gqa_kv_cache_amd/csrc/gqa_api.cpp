@@ -240,6 +240,32 @@ gqa_status hip_fail(hipError_t e, const char* what) {
   return fail(GQA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Combine workgroup shape: enough split lanes that each thread merges at
+// most 16 splits of the longest list (two rounds of 8 loads); with few
+// splits, several rows per workgroup, with many, a slice of the columns
+// (at least 8 quads, so that a row's split lanes stay at lane strides of
+// 8 or more).  cols * rows * quads and the split lanes fill 256 threads.
+// MI355X timings of the combine alone (128K tokens, 128 or 256 splits; 32
+// requests of 8192 tokens at S_q 8, 4-5 splits): a target of 16 splits
+// per thread beat 8 and 4, whose extra workgroups cost more than the
+// second round of loads saves, and beat one workgroup per row (many
+// idle split lanes when splits are few).
+void combine_shape(const gqa_decode_params* p, const gqa_decode_plan& plan, int32_t* cols, int32_t* rows) {
+  const int q4 = p->head_dim / 4;
+  int64_t nsp = plan.num_splits;
+  if (packed_mode(p)) nsp = std::min<int64_t>(nsp, cdiv(std::max(p->max_seqlen_kv, 1), plan.kv_chunk) + 1);
+  int need = 1;
+  while (need * 16 < nsp && need * 8 < gqa::kThreads) need *= 2;
+  int cb = 1, rb = 1;
+  if (need * q4 <= gqa::kThreads) {
+    while (rb < plan.rows && rb * 2 * need * q4 <= gqa::kThreads) rb *= 2;
+  } else {
+    cb = std::min(q4 / 8, need * q4 / gqa::kThreads);
+  }
+  *cols = cb;
+  *rows = rb;
+}
+
 void fill_args(gqa::DecodeArgs& a, const gqa_decode_params* p, const gqa_decode_plan& plan) {
   std::memset(&a, 0, sizeof a);
   a.kv_rows = p->kv_rows;
@@ -270,6 +296,7 @@ void fill_args(gqa::DecodeArgs& a, const gqa_decode_params* p, const gqa_decode_
     a.part_sg = (int64_t)plan.num_splits * plan.rows;
     a.part_ss = plan.rows;
   }
+  combine_shape(p, plan, &a.comb_cols, &a.comb_rows);
   const float scale = p->softmax_scale != 0.f ? p->softmax_scale : 1.0f / std::sqrt((float)p->head_dim);
   a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
 }
@@ -375,7 +402,8 @@ gqa_status gqa_decode_run(const gqa_decode_params* p, const void* q, const void*
                                      static_cast<hipEvent_t>(p->partial_event_end));
   if (e != hipSuccess) return hip_fail(e, "partial kernel launch");
   if (plan.combine) {
-    e = gqa::launch_combine(a, p->head_dim, dim3(plan.rows, p->h_kv, p->batch), s);
+    const int64_t xblocks = cdiv(plan.rows, a.comb_rows) * a.comb_cols;
+    e = gqa::launch_combine(a, p->head_dim, dim3((unsigned)xblocks, p->h_kv, p->batch), s);
     if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
   }
   return GQA_OK;

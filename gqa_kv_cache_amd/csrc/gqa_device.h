@@ -58,6 +58,7 @@ struct DecodeArgs {
   int32_t chunk, num_splits;
   int32_t heads_per_wg;       // KV heads one partial workgroup covers (1, 2 or 4)
   int32_t packed;             // 1: ragged cache split into equal row chunks (split s = chunk s)
+  int32_t comb_cols, comb_rows;  // combine: column slices per row, rows per workgroup
   float scale_log2;           // softmax scale * log2(e)
 };
 
@@ -172,6 +173,17 @@ constexpr int kDppRor4 = 0x124, kDppRor8 = 0x128;
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
   return __builtin_amdgcn_update_dpp(0.0f, x, CTRL, 0xF, 0xF, false);
+}
+
+// Max / sum with lane l ^ st, st = 8, 16 or 32 (row_ror:8 is l ^ 8 inside
+// a row of 16 lanes).
+__device__ __forceinline__ float max_lanes_xor(float x, int st) {
+  if (st == 8) return fmaxf(x, dpp<0x128>(x));
+  return st == 16 ? max_xor16(x) : max_xor32(x);
+}
+__device__ __forceinline__ float sum_lanes_xor(float x, int st) {
+  if (st == 8) return x + dpp<0x128>(x);
+  return st == 16 ? sum_xor16(x) : sum_xor32(x);
 }
 
 // Sum over the CPR lanes l ^ m (m < CPR; CPR = 4, 8 or 16 consecutive

@@ -885,20 +885,31 @@ __global__ void __launch_bounds__(kPThreads, (partial_min_blocks<D, FP8, MB, RV,
   }
 }
 
-// LSE combine: one workgroup per (query row of the group, KV head, request).
-// With M = max_s lse_s (base 2), O = sum_s 2^(lse_s - M) o_s / sum_s 2^(lse_s - M)
-// and LSE = ln 2 * (M + log2 sum_s 2^(lse_s - M)); empty splits (-inf) weigh 0.
-// Thread (column quad d4, split lane sg) owns splits sg, sg + SG, ...; it
+// LSE combine.  With M = max_s lse_s (base 2),
+// O = sum_s 2^(lse_s - M) o_s / sum_s 2^(lse_s - M) and
+// LSE = ln 2 * (M + log2 sum_s 2^(lse_s - M)); empty splits (-inf) weigh 0.
+// A workgroup takes rows [rb * (x / cb), +rb) of one (KV head, request) and
+// column slice x % cb (D / cb columns); its threads are (split lane sg, row,
+// column quad), the column quad fastest, so a wave-wide load reads whole
+// 16-quad runs of a partial row.  Thread sg owns splits sg, sg + SG, ...: it
 // issues all their loads at once and merges them with a private running
-// maximum, and the split lanes are merged once through LDS.
+// maximum.  The split lanes inside a wave are then merged with cross-lane
+// swaps, and the (at most four) wave results through LDS.  The host sizes
+// rb, cb (and so SG) so that a thread has at most 16 splits.
 template <int D>
 __global__ void __launch_bounds__(kThreads) gqa_combine_kernel(DecodeArgs a) {
-  constexpr int Q4 = D / 4;          // float4 columns
-  constexpr int SG = kThreads / Q4;  // split lanes
   constexpr int UNROLL = 8;          // splits per thread per round
-  __shared__ f32x4 racc[SG][Q4];
-  __shared__ float rm[SG], rl[SG];
-  const int r = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  __shared__ f32x4 racc[kThreads];
+  __shared__ float rm[kThreads], rsum[kThreads];
+  const int cb = a.comb_cols, rb = a.comb_rows;
+  const int q4c = D / 4 / cb;        // column quads per workgroup (8 or more)
+  const int W = rb * q4c;            // (row, quad) items, a power of two
+  const int SG = kThreads / W;       // split lanes
+  const int tid = threadIdx.x;
+  const int d4 = (blockIdx.x % cb) * q4c + tid % q4c;
+  const int r = (blockIdx.x / cb) * rb + (tid / q4c) % rb;
+  const int sg = tid / W;
+  const int g = blockIdx.y, b = blockIdx.z;
   const int n = seq_len(a, b);
   // Splits [s_lo, s_lo + nsp) of request b.  Packed: the chunks its rows
   // meet; a request inside one chunk was finished by the partial kernel.
@@ -913,11 +924,10 @@ __global__ void __launch_bounds__(kThreads) gqa_combine_kernel(DecodeArgs a) {
   } else {
     nsp = min(a.num_splits, (list_len(a, n) + a.chunk - 1) / a.chunk);
   }
-  const int64_t first = b * a.part_sb + g * a.part_sg + s_lo * a.part_ss + r;
+  const bool live = r < a.rows;
+  const int64_t first = b * a.part_sb + g * a.part_sg + s_lo * a.part_ss + (live ? r : 0);
   const float* lsep = a.lse_part + first;
   const float* op = a.o_part + first * D;
-  const int d4 = threadIdx.x % Q4;
-  const int sg = threadIdx.x / Q4;
 
   float m = -INFINITY, l = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -936,44 +946,65 @@ __global__ void __launch_bounds__(kThreads) gqa_combine_kernel(DecodeArgs a) {
     float mx = m;
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) mx = fmaxf(mx, ls[u]);
-    if (mx != -INFINITY) {
-      const float alpha = fast_exp2(m - mx);
-      acc *= alpha;
-      l *= alpha;
+    // No branch on mx: a branch lets the compiler sink the row loads below
+    // the LSE loads' wait.  Splits in [0, nsp) hold finite rows (an empty
+    // one holds zeros), so a zero weight contributes exactly zero.
+    const float mref = mx == -INFINITY ? 0.f : mx;
+    const float alpha = fast_exp2(m - mref);
+    acc *= alpha;
+    l *= alpha;
 #pragma unroll
-      for (int u = 0; u < UNROLL; ++u) {
-        const float w = fast_exp2(ls[u] - mx);
-        l += w;
-        acc += w * x[u];
-      }
-      m = mx;
+    for (int u = 0; u < UNROLL; ++u) {
+      const float w = fast_exp2(ls[u] - mref);
+      l += w;
+      acc += w * x[u];
     }
+    m = mx;
   }
-  racc[sg][d4] = acc;
-  if (d4 == 0) {
-    rm[sg] = m;
-    rl[sg] = l;
+
+  // Split lanes of one item inside a wave sit at lane strides W .. 32.
+  float M = m;
+  for (int st = W; st < 64; st *= 2) M = max_lanes_xor(M, st);
+  {
+    const float w = (M == -INFINITY) ? 0.f : fast_exp2(m - M);
+    l *= w;
+    acc *= w;
   }
-  __syncthreads();
-  if (sg != 0) return;
-  float M = -INFINITY;
+  for (int st = W; st < 64; st *= 2) {
+    l = sum_lanes_xor(l, st);
 #pragma unroll
-  for (int k = 0; k < SG; ++k) M = fmaxf(M, rm[k]);
+    for (int c = 0; c < 4; ++c) acc[c] = sum_lanes_xor(acc[c], st);
+  }
+  // Wave results: item t's copies are at t + k * max(W, 64).
+  const int layer = W > 64 ? W : 64;
+  const int K = kThreads / layer;
+  if (K > 1) {
+    racc[tid] = acc;
+    rm[tid] = M;
+    rsum[tid] = l;
+    __syncthreads();
+    if (tid >= W) return;
+    float MM = -INFINITY;
+    for (int k = 0; k < K; ++k) MM = fmaxf(MM, rm[tid + k * layer]);
+    l = 0.f;
+    acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (MM != -INFINITY) {
+      for (int k = 0; k < K; ++k) {
+        const float w = fast_exp2(rm[tid + k * layer] - MM);
+        l += w * rsum[tid + k * layer];
+        acc += w * racc[tid + k * layer];
+      }
+    }
+    M = MM;
+  }
+  if (sg != 0 || !live) return;
   float o[4] = {0.f, 0.f, 0.f, 0.f};
   float lse2 = -INFINITY;
   if (M != -INFINITY) {
-    float S = 0.f;
-    f32x4 t = {0.f, 0.f, 0.f, 0.f};
+    const float inv = 1.f / l;
 #pragma unroll
-    for (int k = 0; k < SG; ++k) {
-      const float w = fast_exp2(rm[k] - M);
-      S += w * rl[k];
-      t += w * racc[k][d4];
-    }
-    const float inv = 1.f / S;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) o[c] = t[c] * inv;
-    lse2 = M + __log2f(S);
+    for (int c = 0; c < 4; ++c) o[c] = acc[c] * inv;
+    lse2 = M + __log2f(l);
   }
   const int i = r / a.group;
   const int h = g * a.group + (r - i * a.group);
