@@ -14,6 +14,14 @@ move (K/V + Q + O + LSE + lengths) divided by the measured time per call,
 the roofline of the partial kernel (algorithmic K/V bytes per launch over
 its event-timed duration, against 8 TB/s), and the CPU oracle timed on a
 bounded sample of the same workload.  Progress goes to stderr.
+
+    python bench.py --op append [--workload append_decode|append_prefill]
+                    [--scale-policy given|first_block]
+
+times the K/V append with FP8 quantisation on write instead: a step is one
+append of every request's new rows into the paged FP8 pool; the line
+reports GB/s over the bytes the append must move (bf16 rows read, codes
+written) and the append kernel's roofline.
 """
 
 from __future__ import annotations
@@ -147,9 +155,13 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="long128k",
+    ap.add_argument("--op", default="decode", choices=["decode", "append"])
+    ap.add_argument("--workload", default=None,
                     choices=["tiny", "long128k", "ragged", "ragged_sq8", "paged", "sparse_fp8",
-                             "long_32x8", "long_8x1", "long_64x8_d64", "long_32x2_d256"])
+                             "long_32x8", "long_8x1", "long_64x8_d64", "long_32x2_d256",
+                             "append_decode", "append_prefill"])
+    ap.add_argument("--scale-policy", default=None, choices=["given", "first_block"],
+                    help="append: scale policy (default: the workload's)")
     ap.add_argument("--kv-chunk", type=int, default=0, help="force list positions per workgroup")
     ap.add_argument("--math", default="auto", choices=["auto", "mfma", "valu"],
                     help="math path of the partial kernel (auto: the planner's measured choice)")
@@ -176,6 +188,13 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     G.load_library()
+    if args.op == "append":
+        return bench_append(args)
+    if args.workload is None:
+        args.workload = "long128k"
+    if args.workload.startswith("append_"):
+        print("append workloads need --op append", file=sys.stderr)
+        sys.exit(2)
 
     say(f"generating workload {args.workload}")
     t = time.perf_counter()
@@ -296,19 +315,7 @@ def main():
         extra["us_per_call_graph"] = round((time.perf_counter() - t) / K * 1e6, 3)
         del graph
     if args.calibrate_copy:
-        src = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(10):
-            dst.copy_(src)
-        b.record(stream)
-        torch.cuda.synchronize()
-        t_copy = a.elapsed_time(b) / 10 * 1e-3
-        extra["d2d_copy_512MiB_GBps"] = round(2 * (512 << 20) / t_copy / 1e9, 1)
-        del src, dst
+        extra["d2d_copy_512MiB_GBps"] = calibrate_copy(torch, stream)
 
     traffic = read_traffic(args.workload)
     line = {
@@ -358,6 +365,187 @@ def main():
     if not ok:
         say("GPU output does not match the oracle on the sampled rows")
         sys.exit(1)
+
+
+def calibrate_copy(torch, stream) -> float:
+    """A 512 MiB device-to-device copy (its counters scale FETCH_SIZE /
+    WRITE_SIZE of the same profiled run); returns its GB/s."""
+    src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(10):
+        dst.copy_(src)
+    b.record(stream)
+    torch.cuda.synchronize()
+    t_copy = a.elapsed_time(b) / 10 * 1e-3
+    del src, dst
+    return round(2 * (512 << 20) / t_copy / 1e9, 1)
+
+
+APPEND_METRIC = "GB/s over the bytes moved, K/V append with FP8 quantise-on-write (paged pool)"
+
+
+def bench_append(args):
+    """One step = one gqa_kv_append of every request's new rows."""
+    import torch
+
+    import gqa_inputs as gi
+    import gqa_kv_cache_amd as G
+
+    name = args.workload or "append_decode"
+    if not name.startswith("append_"):
+        print("--op append takes --workload append_decode or append_prefill", file=sys.stderr)
+        sys.exit(2)
+    say(f"generating append workload {name}")
+    w = gi.append_named(name)
+    policy = args.scale_policy or w.policy
+    B, S, Hkv, d = w.k_new.shape
+    P, pps = w.page_size, w.block_table.shape[1]
+    dev = "cuda"
+    elems = B * S * Hkv * d
+    bf16 = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev)
+    kn, vn = bf16(w.k_new), bf16(w.v_new)
+    kc = torch.zeros((w.pool_pages, P, Hkv, d), dtype=torch.uint8, device=dev)
+    vc = torch.zeros_like(kc)
+    sl = torch.from_numpy(w.seqlens).to(dev)
+    so = torch.empty_like(sl)
+    bt = torch.from_numpy(w.block_table).to(dev)
+    ks = torch.from_numpy(w.k_scale).to(dev)
+    vs = torch.from_numpy(w.v_scale).to(dev)
+    p = G.make_append_params(batch=B, s_new=S, h_kv=Hkv, head_dim=d, layout="paged", kv_dtype="fp8_e4m3fn",
+                             scale_policy=policy, kv_rows=w.pool_pages * P, page_size=P, max_pages_per_seq=pps)
+    wsb = G.gqa_kv_append_workspace_size(p)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        G.gqa_kv_append(p, kn, vn, sl, so, bt, kc, vc, ks, vs, ws, wsb, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    say(f"timing {K} appends ({B} x {S} rows, policy {policy})")
+    t0 = time.perf_counter()
+    for _ in range(K):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    # Per-call device time: events around each call on the launch stream
+    # (with the given policy a call is one dispatch of the append kernel).
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for a, b in ev:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    dev_us = statistics.mean(a.elapsed_time(b) for a, b in ev) * 1e3
+    two_pass = wsb > 0
+    # bytes: bf16 K and V read, codes written, lengths and scales; the
+    # first-block policy over several workgroups reads the rows twice
+    pages_touched = B * (-(-S // P) + 1)
+    min_bytes = elems * 2 * (2 + 1) + B * 4 * 2 + B * Hkv * 4 * 2 + pages_touched * 4
+    alg = elems * 2 * (2 + 1) + (elems * 2 * 2 if two_pass else 0)
+    us_per_call = wall / K * 1e6
+    value = min_bytes / (us_per_call * 1e-6) / 1e9
+    achieved = alg / (dev_us * 1e-6) / 1e9
+    say(f"  {us_per_call:.2f} us/call, device {dev_us:.2f} us, {value:.1f} GB/s, kernel {achieved:.1f} GB/s")
+    extra = {}
+    if args.calibrate_copy:
+        extra["d2d_copy_512MiB_GBps"] = calibrate_copy(torch, stream)
+
+    line = {
+        "metric": APPEND_METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / K * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16->fp8_e4m3fn",
+        "data": "synthetic",
+        "config": {"workload": name, "batch": B, "new_tokens": S, "h_kv": Hkv, "head_dim": d,
+                   "stored_tokens": int(w.seqlens[0]), "layout": "paged", "page_size": P,
+                   "scale_policy": policy, "seed": w.seed, "passes": 2 if two_pass else 1},
+        "us_per_call": round(us_per_call, 3),
+        "min_bytes_per_call": int(min_bytes),
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "gqa_append_kernel" + (" (absmax pass + write pass)" if two_pass else ""),
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+            "algorithmic_bytes_per_launch": int(alg),
+            "kernel_us": round(dev_us, 3),
+        },
+        **extra,
+    }
+    ok = True
+    if not args.no_cpu_baseline:
+        say("timing the CPU append oracle on a bounded sample and checking sampled requests")
+        res, chk = append_baseline_and_check(w, policy, kc, vc, ks, vs, so)
+        line["cpu_baseline"] = res
+        line["check"] = chk
+        ok = chk["ok"]
+    print(json.dumps(line), flush=True)
+    if not ok:
+        say("GPU append does not match the oracle on the sampled requests")
+        sys.exit(1)
+
+
+def append_baseline_and_check(w, policy, kc, vc, ks, vs, so, budget_s: float = 10.0):
+    """Run the append oracle request by request (each on a compact pool of
+    its own pages) until about budget_s of CPU time; time it, and compare
+    every byte of those requests' pages and their scales with the GPU's."""
+    from oracle import append as A
+
+    B, S, Hkv, d = w.k_new.shape
+    P, pps = w.page_size, w.block_table.shape[1]
+    gk, gv = kc.cpu().numpy(), vc.cpu().numpy()
+    gks, gvs, gso = ks.cpu().numpy(), vs.cpu().numpy(), so.cpu().numpy()
+    done, t_oracle, ok = 0, 0.0, True
+    mism = 0
+    for b in range(B):
+        pages = w.block_table[b]
+        bt = np.arange(pps, dtype=np.int32)[None, :]
+        zero = np.zeros((pps, P, Hkv, d), np.uint8)
+        t = time.perf_counter()
+        ok_k, ok_v, rks, rvs, lens = A.reference_append(
+            k_cache=zero, v_cache=zero, k_new=w.k_new[b:b + 1], v_new=w.v_new[b:b + 1],
+            seqlens=w.seqlens[b:b + 1], layout="paged", kv_dtype="fp8_e4m3fn", block_table=bt, page_size=P,
+            k_scale=w.k_scale[b:b + 1], v_scale=w.v_scale[b:b + 1], policy=policy)
+        t_oracle += time.perf_counter() - t
+        n0 = int(w.seqlens[b])
+        # only the appended slots are compared (the pool's other slots keep
+        # whatever the GPU pool held)
+        for j in range(S):
+            tok = n0 + j
+            pg, sl = tok // P, tok % P
+            if pg >= pps:
+                continue
+            if not (np.array_equal(gk[pages[pg], sl], ok_k[pg, sl]) and np.array_equal(gv[pages[pg], sl], ok_v[pg, sl])):
+                mism += 1
+        if not (np.array_equal(gks[b], rks[0]) and np.array_equal(gvs[b], rvs[0]) and gso[b] == lens[0]):
+            mism += 1
+        done += 1
+        if t_oracle >= budget_s:
+            break
+    ok = mism == 0
+    rows = done * S
+    moved = rows * Hkv * d * 2 * 3
+    res = {"value": round(moved / t_oracle / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+           "sample": f"{done} of {B} requests ({rows} of {B * S} new rows), {t_oracle:.1f} s on {platform.machine()}",
+           "seconds": round(t_oracle, 2)}
+    return res, {"requests": done, "mismatches": mism, "ok": bool(ok)}
 
 
 if __name__ == "__main__":

@@ -313,3 +313,53 @@ def named(name: str) -> Workload:
 def scaled(spec: Spec, **changes) -> Spec:
     """A smaller copy of a named spec (same heads, d, layout and dtype)."""
     return dataclasses.replace(spec, **changes)
+
+
+# ---------------------------------------------------------------------------
+# K/V append inputs: the new rows a model step produces, and the paged pool
+# they are written into.
+# ---------------------------------------------------------------------------
+
+STREAM_SCALES = 7
+
+
+@dataclasses.dataclass
+class AppendWorkload:
+    name: str
+    seed: int
+    k_new: np.ndarray          # uint16 bf16 bits [B, S, H_kv, d]
+    v_new: np.ndarray
+    seqlens: np.ndarray        # int32 [B], lengths before the append
+    block_table: np.ndarray    # int32 [B, pages_per_seq]
+    pool_pages: int
+    page_size: int
+    k_scale: np.ndarray        # float32 [B, H_kv] (used by the given-scale policy)
+    v_scale: np.ndarray
+    policy: str                # "given" or "first_block"
+
+
+# name: (batch, new tokens, H_kv, d, existing tokens, pages per request, policy, seed)
+APPEND_NAMED = {
+    # one decode step of the sparse FP8 workload's cache: token 512 of each
+    # of 256 requests (511 stored), 8 KV heads, d 128, pages of 16
+    "append_decode": (256, 1, 8, 128, 511, 32, "given", 10),
+    # a prefill-sized append: 32 empty requests receive 8192 rows each
+    # (the ragged S_q 8 batch's cache), scales from the block
+    "append_prefill": (32, 8192, 8, 128, 0, 512, "first_block", 11),
+}
+
+
+def append_named(name: str) -> AppendWorkload:
+    B, S, Hkv, d, n0, pps, policy, seed = APPEND_NAMED[name]
+    P = 16
+    k_new = normal_bf16_bits(stream_rng(seed, STREAM_K), (B, S, Hkv, d))
+    v_new = normal_bf16_bits(stream_rng(seed, STREAM_V), (B, S, Hkv, d))
+    pool = B * pps
+    bt = stream_rng(seed, STREAM_PAGES).permutation(pool).reshape(B, pps).astype(np.int32)
+    # given scales: an absmax/448-sized scale for N(0, 1) rows, per (request, head)
+    rs = stream_rng(seed, STREAM_SCALES)
+    ks = (rs.uniform(4.0, 5.0, size=(B, Hkv)) / E4M3FN_MAX).astype(np.float32)
+    vs = (rs.uniform(4.0, 5.0, size=(B, Hkv)) / E4M3FN_MAX).astype(np.float32)
+    return AppendWorkload(name=name, seed=seed, k_new=k_new, v_new=v_new,
+                          seqlens=np.full(B, n0, dtype=np.int32), block_table=bt, pool_pages=pool,
+                          page_size=P, k_scale=ks, v_scale=vs, policy=policy)

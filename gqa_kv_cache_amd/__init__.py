@@ -2,16 +2,19 @@
 
 Argument marshalling only: every step of the computation runs in the HIP
 kernels of ``libgqa_decode.so``.  torch supplies device memory and the
-current stream.  The names mirror the C ABI in ``include/gqa_decode.h``:
+current stream.  The names mirror the C ABI in ``include/gqa_decode.h``
+and ``include/gqa_append.h``:
 
     gqa_decode_make_plan(params)              -> dict
     gqa_decode_workspace_size(params)         -> int
     gqa_decode_run(params, q, k_cache, ...)   -> None (writes o, lse)
     gqa_resolve_rows(params, ..., rows_out)   -> None
+    gqa_kv_append_workspace_size(aparams)     -> int
+    gqa_kv_append(aparams, k_new, v_new, ...) -> None (writes the cache rows)
     gqa_status_string(code), gqa_abi_version()
 
-plus ``make_params(...)`` and a convenience ``decode(...)`` that allocates
-the outputs and workspace with torch.  There is no fallback: if the library
+plus ``make_params(...)`` / ``make_append_params(...)`` and a convenience
+``decode(...)`` that allocates the outputs and workspace with torch.  There is no fallback: if the library
 is missing or fails to load, every call raises.
 """
 
@@ -32,6 +35,7 @@ LAYOUTS = {"contiguous": LAYOUT_CONTIGUOUS, "ragged": LAYOUT_RAGGED, "paged": LA
 KV_DTYPES = {"bf16": KV_BF16, "fp8_e4m3fn": KV_FP8_E4M3FN}
 GATE_MODES = {"none": GATE_NONE, "elementwise": GATE_ELEMENTWISE, "headwise": GATE_HEADWISE}
 MATH = {"auto": 0, "mfma": 1, "valu": 2}
+SCALE_POLICIES = {"given": 0, "first_block": 1}
 
 STATUS = {0: "GQA_OK", 1: "GQA_ERR_INVALID_ARG", 2: "GQA_ERR_UNSUPPORTED", 3: "GQA_ERR_ALIGNMENT",
           4: "GQA_ERR_WORKSPACE", 5: "GQA_ERR_HIP"}
@@ -64,6 +68,16 @@ class Plan(ctypes.Structure):
     ]
 
 
+class AppendParams(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("s_new", ctypes.c_int32), ("h_kv", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("layout", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
+        ("scale_policy", ctypes.c_int32), ("seq_capacity", ctypes.c_int32), ("kv_rows", ctypes.c_int64),
+        ("page_size", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32),
+        ("reserved", ctypes.c_int32 * 4),
+    ]
+
+
 _lib_handle = None
 
 
@@ -83,7 +97,11 @@ def load_library(path: Optional[str] = None):
     lib.gqa_decode_workspace_size.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
     lib.gqa_decode_run.argtypes = [P] + [vp] * 13 + [ctypes.c_size_t, vp]
     lib.gqa_resolve_rows.argtypes = [P, vp, vp, vp, vp, vp, vp]
-    for f in ("gqa_decode_make_plan", "gqa_decode_workspace_size", "gqa_decode_run", "gqa_resolve_rows"):
+    A = ctypes.POINTER(AppendParams)
+    lib.gqa_kv_append_workspace_size.argtypes = [A, ctypes.POINTER(ctypes.c_size_t)]
+    lib.gqa_kv_append.argtypes = [A] + [vp] * 10 + [ctypes.c_size_t, vp]
+    for f in ("gqa_decode_make_plan", "gqa_decode_workspace_size", "gqa_decode_run", "gqa_resolve_rows",
+              "gqa_kv_append_workspace_size", "gqa_kv_append"):
         getattr(lib, f).restype = ctypes.c_int
     lib.gqa_status_string.argtypes = [ctypes.c_int]
     lib.gqa_status_string.restype = ctypes.c_char_p
@@ -187,6 +205,42 @@ def gqa_resolve_rows(params: Params, seqlens=None, cu_seqlens=None, block_table=
     lib = load_library()
     st = lib.gqa_resolve_rows(ctypes.byref(params), _ptr(seqlens), _ptr(cu_seqlens), _ptr(block_table),
                               _ptr(topk_idx), _ptr(rows_out), _stream_handle(stream))
+    _check(lib, st)
+
+
+def make_append_params(*, batch: int, s_new: int, h_kv: int, head_dim: int, layout="paged",
+                       kv_dtype="fp8_e4m3fn", scale_policy="given", seq_capacity: int = 0,
+                       kv_rows: int, page_size: int = 16, max_pages_per_seq: int = 0) -> AppendParams:
+    p = AppendParams()
+    p.batch, p.s_new, p.h_kv, p.head_dim = batch, s_new, h_kv, head_dim
+    p.layout = LAYOUTS[layout] if isinstance(layout, str) else int(layout)
+    p.kv_dtype = KV_DTYPES[kv_dtype] if isinstance(kv_dtype, str) else int(kv_dtype)
+    p.scale_policy = SCALE_POLICIES[scale_policy] if isinstance(scale_policy, str) else int(scale_policy)
+    p.seq_capacity = seq_capacity
+    p.kv_rows = kv_rows
+    p.page_size = page_size
+    p.max_pages_per_seq = max_pages_per_seq
+    return p
+
+
+def gqa_kv_append_workspace_size(params: AppendParams) -> int:
+    lib = load_library()
+    n = ctypes.c_size_t(0)
+    _check(lib, lib.gqa_kv_append_workspace_size(ctypes.byref(params), ctypes.byref(n)))
+    return int(n.value)
+
+
+def gqa_kv_append(params: AppendParams, k_new, v_new, seqlens, seqlens_out=None, block_table=None,
+                  k_cache=None, v_cache=None, k_scale=None, v_scale=None, workspace=None,
+                  workspace_bytes: Optional[int] = None, stream=None) -> None:
+    """Enqueue one append: the new rows go after each request's length."""
+    lib = load_library()
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None else (
+            workspace.numel() * workspace.element_size() if not isinstance(workspace, int) else 0)
+    st = lib.gqa_kv_append(ctypes.byref(params), _ptr(k_new), _ptr(v_new), _ptr(seqlens), _ptr(seqlens_out),
+                           _ptr(block_table), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+                           _ptr(workspace), ctypes.c_size_t(workspace_bytes), _stream_handle(stream))
     _check(lib, st)
 
 

@@ -13,6 +13,8 @@
 #include <mutex>
 #include <string>
 
+#include "gqa_append.h"
+#include "gqa_append_args.h"
 #include "gqa_decode.h"
 #include "gqa_device.h"
 
@@ -301,6 +303,48 @@ void fill_args(gqa::DecodeArgs& a, const gqa_decode_params* p, const gqa_decode_
   a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
 }
 
+// ---- K/V append --------------------------------------------------------
+
+gqa_status check_append(const gqa_append_params* p) {
+  if (!p) return fail(GQA_ERR_INVALID_ARG, "params is NULL");
+  if (p->batch < 0 || p->s_new < 1) return fail(GQA_ERR_INVALID_ARG, "batch must be >= 0 and s_new >= 1");
+  if (p->h_kv < 1 || p->h_kv > gqa::kAppendMaxHeads)
+    return fail(GQA_ERR_UNSUPPORTED, "h_kv must be 1..%d", gqa::kAppendMaxHeads);
+  if (p->head_dim != 64 && p->head_dim != 128 && p->head_dim != 256)
+    return fail(GQA_ERR_UNSUPPORTED, "head_dim %d not built (64, 128, 256)", p->head_dim);
+  if (p->kv_dtype != GQA_KV_BF16 && p->kv_dtype != GQA_KV_FP8_E4M3FN) return fail(GQA_ERR_INVALID_ARG, "bad kv_dtype");
+  if (p->scale_policy != GQA_SCALE_GIVEN && p->scale_policy != GQA_SCALE_FIRST_BLOCK)
+    return fail(GQA_ERR_INVALID_ARG, "bad scale_policy");
+  if (p->kv_rows < 1) return fail(GQA_ERR_INVALID_ARG, "kv_rows must be >= 1");
+  for (int r : p->reserved)
+    if (r != 0) return fail(GQA_ERR_INVALID_ARG, "reserved fields must be 0");
+  if (p->layout == GQA_LAYOUT_CONTIGUOUS) {
+    if (p->seq_capacity < 1) return fail(GQA_ERR_INVALID_ARG, "contiguous layout needs seq_capacity >= 1");
+    if ((int64_t)p->batch * p->seq_capacity > p->kv_rows)
+      return fail(GQA_ERR_INVALID_ARG, "batch * seq_capacity exceeds kv_rows");
+  } else if (p->layout == GQA_LAYOUT_PAGED) {
+    if (p->page_size < 1 || p->page_size > 1024 || log2_exact(p->page_size) < 0)
+      return fail(GQA_ERR_INVALID_ARG, "page_size must be a power of two in 1..1024");
+    if (p->max_pages_per_seq < 1) return fail(GQA_ERR_INVALID_ARG, "paged layout needs max_pages_per_seq >= 1");
+  } else {
+    return fail(GQA_ERR_UNSUPPORTED, "append writes contiguous or paged caches (a packed ragged cache has no room)");
+  }
+  return GQA_OK;
+}
+
+// New tokens per append workgroup: as many as fit kAppendElemsPerWorkgroup
+// elements (all KV heads of a token together), at least one.
+int append_chunk_tokens(const gqa_append_params* p) {
+  const int fit = std::max(1, gqa::kAppendElemsPerWorkgroup / (p->h_kv * p->head_dim));
+  return std::min(fit, p->s_new);
+}
+
+size_t append_workspace(const gqa_append_params* p) {
+  const int chunks = (int)cdiv(p->s_new, append_chunk_tokens(p));
+  if (p->kv_dtype != GQA_KV_FP8_E4M3FN || p->scale_policy != GQA_SCALE_FIRST_BLOCK || chunks == 1) return 0;
+  return (size_t)p->batch * chunks * 2 * p->h_kv * sizeof(uint32_t);
+}
+
 }  // namespace
 
 extern "C" {
@@ -434,6 +478,72 @@ gqa_status gqa_resolve_rows(const gqa_decode_params* p, const int32_t* seqlens, 
   a.topk = topk_idx;
   hipError_t e = gqa::launch_resolve(a, rows_out, list_cap, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "resolve kernel launch");
+  return GQA_OK;
+}
+
+gqa_status gqa_kv_append_workspace_size(const gqa_append_params* p, size_t* bytes) {
+  g_last_error.clear();
+  gqa_status st = check_append(p);
+  if (st != GQA_OK) return st;
+  if (!bytes) return fail(GQA_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = append_workspace(p);
+  return GQA_OK;
+}
+
+gqa_status gqa_kv_append(const gqa_append_params* p, const void* k_new, const void* v_new,
+                         const int32_t* seqlens, int32_t* seqlens_out, const int32_t* block_table,
+                         void* k_cache, void* v_cache, float* k_scale, float* v_scale, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  gqa_status st = check_append(p);
+  if (st != GQA_OK) return st;
+  if (!k_new || !v_new || !seqlens || !k_cache || !v_cache)
+    return fail(GQA_ERR_INVALID_ARG, "k_new, v_new, seqlens, k_cache and v_cache are required");
+  if (seqlens_out && seqlens_out == seqlens)
+    return fail(GQA_ERR_INVALID_ARG, "seqlens_out must not alias seqlens");
+  if (p->layout == GQA_LAYOUT_PAGED && !block_table) return fail(GQA_ERR_INVALID_ARG, "paged layout needs block_table");
+  const bool fp8 = p->kv_dtype == GQA_KV_FP8_E4M3FN;
+  if (fp8 && (!k_scale || !v_scale)) return fail(GQA_ERR_INVALID_ARG, "FP8 caches need k_scale and v_scale");
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16))
+    return fail(GQA_ERR_ALIGNMENT, "k_new, v_new, k_cache and v_cache must be 16-byte aligned");
+  const void* small[] = {seqlens, seqlens_out, block_table, k_scale, v_scale};
+  for (const void* ptr : small)
+    if (ptr && !aligned(ptr, 4)) return fail(GQA_ERR_ALIGNMENT, "length, block-table and scale arrays must be 4-byte aligned");
+  const size_t need = append_workspace(p);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need)
+      return fail(GQA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : (size_t)0);
+    if (!aligned(workspace, 4)) return fail(GQA_ERR_ALIGNMENT, "workspace must be 4-byte aligned");
+  }
+  if (p->batch == 0) return GQA_OK;
+
+  gqa::AppendArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.k_new = static_cast<const uint16_t*>(k_new);
+  a.v_new = static_cast<const uint16_t*>(v_new);
+  a.seqlens = seqlens;
+  a.seqlens_out = seqlens_out;
+  a.block_table = block_table;
+  a.k_cache = static_cast<uint8_t*>(k_cache);
+  a.v_cache = static_cast<uint8_t*>(v_cache);
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.amax = static_cast<uint32_t*>(workspace);
+  a.kv_rows = p->kv_rows;
+  a.batch = p->batch;
+  a.s_new = p->s_new;
+  a.h_kv = p->h_kv;
+  a.head_dim = p->head_dim;
+  a.paged = p->layout == GQA_LAYOUT_PAGED;
+  a.fp8 = fp8;
+  a.first_block = p->scale_policy == GQA_SCALE_FIRST_BLOCK;
+  a.seq_cap = p->seq_capacity;
+  a.page_shift = a.paged ? log2_exact(p->page_size) : 0;
+  a.max_pages = p->max_pages_per_seq;
+  a.chunk_tokens = append_chunk_tokens(p);
+  a.chunks = (int32_t)cdiv(p->s_new, a.chunk_tokens);
+  hipError_t e = gqa::launch_append(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "append kernel launch");
   return GQA_OK;
 }
 

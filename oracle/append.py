@@ -30,7 +30,10 @@ What the pages fix, and what is read into them:
   what falls outside +-448 * scale.  Stored codes are never re-scaled.
 * Rows go to logical positions n_b .. n_b + S - 1 of request b, through the
   same physical-row map the decode path reads (contiguous or paged), and
-  the new length is n_b + S.
+  the new length is n_b + S.  A position with no row of its own -- past
+  the request's capacity (contiguous), past its block-table row (paged),
+  or mapped outside the cache -- is not written (the library's contract;
+  the pages say nothing about overflow).
 
 Parity pins live in ``tests/test_oracle_append.py``.
 """
@@ -81,7 +84,8 @@ def e4m3fn_encode(y: np.ndarray) -> np.ndarray:
 def quantize(x_f32: np.ndarray, scale: float) -> np.ndarray:
     """FP8 codes of float32 values x under one scale: float32 quotient,
     clamp to +-448, round to nearest even."""
-    y = np.asarray(x_f32, dtype=np.float32) / np.float32(scale)
+    with np.errstate(over="ignore"):          # an infinite quotient saturates below
+        y = np.asarray(x_f32, dtype=np.float32) / np.float32(scale)
     y = np.clip(y, np.float32(-E4M3FN_MAX), np.float32(E4M3FN_MAX))
     return e4m3fn_encode(y.astype(np.float64))
 
@@ -133,7 +137,14 @@ def reference_append(*, k_cache, v_cache, k_new, v_new, seqlens, layout: str, kv
                         sc[b, g] = first_block_scale(x)
                     codes = quantize(x, float(sc[b, g]))
                 for j in range(S):
-                    r = physical_row(b, n + j, layout, capacity=capacity, block_table=block_table,
+                    t = n + j
+                    if t < 0 or (layout == CONTIGUOUS and t >= capacity):
+                        continue
+                    if layout == PAGED and t // page_size >= np.asarray(block_table).shape[1]:
+                        continue
+                    r = physical_row(b, t, layout, capacity=capacity, block_table=block_table,
                                      page_size=page_size)
+                    if not 0 <= r < rows.shape[0]:
+                        continue
                     rows[r, g, :] = codes[j] if kv_dtype == FP8 else block[j]
     return kc, vc, ks, vs, (lens + S).astype(np.int32)

@@ -10,29 +10,33 @@ import pytest
 
 import gqa_kv_cache_amd as G
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "gqa_decode.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+HEADERS = sorted(os.path.join(INCLUDE, f) for f in os.listdir(INCLUDE) if f.endswith(".h"))
+
+
+def header_text():
+    return re.sub(r"/\*.*?\*/", "", "\n".join(open(h).read() for h in HEADERS), flags=re.S)
 
 # Fake, aligned device addresses: validation never dereferences pointers.
 A16 = 0x10000
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(gqa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(gqa_[a-z_]+)\s*\(", header_text())))
 
 
 def test_library_exports_every_declared_function():
     lib = G.load_library()
     names = declared_functions()
     assert {"gqa_decode_run", "gqa_decode_workspace_size", "gqa_decode_make_plan", "gqa_resolve_rows",
-            "gqa_status_string", "gqa_last_error", "gqa_abi_version"} <= set(names)
+            "gqa_status_string", "gqa_last_error", "gqa_abi_version", "gqa_kv_append",
+            "gqa_kv_append_workspace_size"} <= set(names)
     for n in names:
-        assert hasattr(lib, n), f"{n} declared in gqa_decode.h but not exported"
+        assert hasattr(lib, n), f"{n} declared in include/ but not exported"
 
 
 def test_binding_argument_counts_match_header():
-    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    text = header_text()
     lib = G.load_library()
     for name in declared_functions():
         m = re.search(r"\b" + name + r"\s*\((.*?)\)\s*;", text, flags=re.S)
@@ -169,3 +173,65 @@ def test_run_validation_statuses():
 
 def test_run_batch_zero_is_a_no_op():
     assert _run(base(batch=0, kv_rows=1)) == 0
+
+
+# ---- K/V append -----------------------------------------------------------
+
+def append_base(**kw):
+    d = dict(batch=2, s_new=3, h_kv=4, head_dim=128, layout="paged", kv_dtype="fp8_e4m3fn",
+             scale_policy="given", kv_rows=4096, page_size=16, max_pages_per_seq=8)
+    d.update(kw)
+    return G.make_append_params(**d)
+
+
+def _append(p, kn=A16, vn=A16, sl=A16, so=None, bt=A16, kc=A16, vc=A16, ks=A16, vs=A16, ws=None, ws_bytes=0):
+    lib = G.load_library()
+    return lib.gqa_kv_append(ctypes.byref(p), kn, vn, sl, so, bt, kc, vc, ks, vs, ws, ctypes.c_size_t(ws_bytes), None)
+
+
+def test_append_params_layout_matches_header():
+    assert ctypes.sizeof(G.AppendParams) == 64
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(s_new=0), 1), (dict(batch=-1), 1), (dict(h_kv=0), 2), (dict(h_kv=257), 2), (dict(head_dim=96), 2),
+    (dict(kv_dtype=7), 1), (dict(scale_policy=3), 1), (dict(kv_rows=0), 1), (dict(layout="ragged"), 2),
+    (dict(page_size=12), 1), (dict(max_pages_per_seq=0), 1), (dict(layout="contiguous", seq_capacity=0), 1),
+    (dict(layout="contiguous", seq_capacity=4096), 1),   # batch * capacity > kv_rows
+])
+def test_append_rejects_bad_params(kw, status):
+    n = ctypes.c_size_t(0)
+    assert G.load_library().gqa_kv_append_workspace_size(ctypes.byref(append_base(**kw)), ctypes.byref(n)) == status
+    assert _append(append_base(**kw)) == status
+
+
+def test_append_reserved_must_be_zero():
+    p = append_base()
+    p.reserved[2] = 1
+    assert _append(p) == 1
+
+
+def test_append_validation_statuses():
+    p = append_base()
+    assert _append(p, kn=None) == 1
+    assert _append(p, sl=None) == 1
+    assert _append(p, bt=None) == 1                              # paged needs a block table
+    assert _append(p, ks=None) == 1                              # FP8 needs scales
+    assert _append(p, so=A16) == 1                               # seqlens_out aliases seqlens
+    assert _append(p, kc=A16 + 8) == 3
+    assert _append(p, so=A16 + 2) == 3
+
+
+def test_append_workspace_only_for_multi_block_first_block():
+    ws = G.gqa_kv_append_workspace_size
+    assert ws(append_base(scale_policy="first_block")) == 0                 # one workgroup per request
+    assert ws(append_base(scale_policy="given", s_new=5000)) == 0
+    assert ws(append_base(kv_dtype="bf16", scale_policy="first_block", s_new=5000)) == 0
+    need = ws(append_base(scale_policy="first_block", s_new=5000))
+    assert need == 2 * 40 * 2 * 4 * 4           # B x chunks (5000 rows / 128 per workgroup) x (K, V) x H_kv x 4 B
+    assert _append(append_base(scale_policy="first_block", s_new=5000)) == 4
+    assert _append(append_base(scale_policy="first_block", s_new=5000), ws=A16, ws_bytes=need - 4) == 4
+
+
+def test_append_batch_zero_is_a_no_op():
+    assert _append(append_base(batch=0)) == 0
