@@ -143,17 +143,38 @@ def test_append_page_size_one_and_large():
              P=256, pages_per_seq=2, seed=6)
 
 
+def _every_bf16_row():
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    bits[~np.isfinite(A.bf16_bits_to_f32(bits))] = 0       # NaN and infinity replaced by zero
+    return bits
+
+
 @pytest.mark.parametrize("scale", [1.0, 0.125, 0.0137, 3.0])
 def test_encoder_on_every_bf16_value(scale):
     # one token row of 256 heads x d 256 = 65536 elements: every bf16 bit
-    # pattern once (NaN and infinity replaced by zero), under one scale
-    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
-    f = A.bf16_bits_to_f32(bits)
-    bits[~np.isfinite(f)] = 0
-    k_new = bits.reshape(1, 1, 256, 256)
+    # pattern once, under one scale
+    k_new = _every_bf16_row().reshape(1, 1, 256, 256)
     v_new = k_new[:, :, ::-1, ::-1].copy()
     run_case(layout=R.CONTIGUOUS, kv_dtype=R.FP8, policy="given", B=1, S=1, Hkv=256, d=256, lens=[0], cap=2,
              scales=np.full((1, 256), scale, np.float32), k_new=k_new, v_new=v_new)
+
+
+def test_encoder_on_every_bf16_value_under_many_scales():
+    # 32 requests x 256 heads of per-head scales -- log-uniform over 2^-40 ..
+    # 2^40, powers of two (exact quotients, many exact ties), and the ends:
+    # a subnormal scale whose reciprocal overflows, a subnormal one whose
+    # reciprocal does not, and huge ones.  Each request holds every bf16
+    # value once, rotated so that each value meets other heads.
+    B, H, d = 32, 256, 256
+    rng = np.random.default_rng(77)
+    scales = np.exp2(rng.uniform(-40, 40, size=(B, H))).astype(np.float32)
+    scales[0, :64] = np.exp2(np.arange(-32, 32)).astype(np.float32)
+    scales[1, :8] = np.array([1e-40, 5e-39, 1.2e-38, 1e30, 3e38, 1.0, 448.0, 1 / 448], np.float32)
+    row = _every_bf16_row()
+    k_new = np.stack([np.roll(row, 997 * b) for b in range(B)]).reshape(B, 1, H, d)
+    v_new = k_new[:, :, ::-1, ::-1].copy()
+    run_case(layout=R.CONTIGUOUS, kv_dtype=R.FP8, policy="given", B=B, S=1, Hkv=H, d=d, lens=[0] * B, cap=1,
+             scales=scales, k_new=k_new, v_new=v_new)
 
 
 def test_append_then_decode():
