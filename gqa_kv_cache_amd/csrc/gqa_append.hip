@@ -82,6 +82,44 @@ __device__ __forceinline__ uint2 quantize8(const uint4 x, float s, float y, bool
   return uint2{(uint32_t)lo, (uint32_t)hi};
 }
 
+// Absolute maxima of this workgroup's T new tokens, per KV head, into smax
+// (fp32 bits; zeroed by the caller, then a barrier): one head at a time,
+// each thread keeping its own maximum over its items with U loads of K and
+// of V in flight, then a wave reduction and one LDS atomic per wave.
+template <int U>
+__device__ __forceinline__ void block_absmax(const AppendArgs& a, int64_t in_base, int T, uint32_t* smax) {
+  const int d8 = a.head_dim / 8;
+  const int per_head = T * d8;
+  for (int g = 0; g < a.h_kv; ++g) {
+    float mk = 0.f, mv = 0.f;
+    for (int base = 0; base < per_head; base += U * kAppendThreads) {
+      uint4 kx[U], vx[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int it = min(base + u * kAppendThreads + (int)threadIdx.x, per_head - 1);
+        const int j = it / d8;
+        const int64_t off = in_base + ((int64_t)j * a.h_kv + g) * a.head_dim + (it - j * d8) * 8;
+        kx[u] = *reinterpret_cast<const uint4*>(a.k_new + off);
+        vx[u] = *reinterpret_cast<const uint4*>(a.v_new + off);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        mk = fmaxf(mk, absmax8(kx[u]));  // a clamped index repeats a valid item: harmless for a maximum
+        mv = fmaxf(mv, absmax8(vx[u]));
+      }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      mk = fmaxf(mk, __shfl_xor(mk, off));
+      mv = fmaxf(mv, __shfl_xor(mv, off));
+    }
+    if ((threadIdx.x & 63) == 0) {
+      atomicMax(&smax[2 * g], __builtin_bit_cast(uint32_t, mk));  // |x| >= 0: integer order = float order
+      atomicMax(&smax[2 * g + 1], __builtin_bit_cast(uint32_t, mv));
+    }
+  }
+}
+
 // Physical token row of logical token t of request b, or -1 (not written).
 __device__ __forceinline__ int64_t append_row(const AppendArgs& a, int b, int64_t t) {
   if (t < 0) return -1;
@@ -146,14 +184,7 @@ __global__ void __launch_bounds__(kAppendThreads) gqa_append_kernel(AppendArgs a
   if (calib && (PASS == 0 || a.chunks == 1)) {
     for (int i = threadIdx.x; i < 2 * a.h_kv; i += kAppendThreads) smax[i] = 0u;
     __syncthreads();
-    for (int it = threadIdx.x; it < items; it += kAppendThreads) {
-      const int g = (it % per_tok) / d8;
-      const int64_t off = in_base + (int64_t)it * 8;
-      const float mk = absmax8(*reinterpret_cast<const uint4*>(a.k_new + off));
-      const float mv = absmax8(*reinterpret_cast<const uint4*>(a.v_new + off));
-      atomicMax(&smax[2 * g], __builtin_bit_cast(uint32_t, mk));  // |x| >= 0: integer order = float order
-      atomicMax(&smax[2 * g + 1], __builtin_bit_cast(uint32_t, mv));
-    }
+    block_absmax<U>(a, in_base, T, smax);
     __syncthreads();
     if (PASS == 0) {
       for (int i = threadIdx.x; i < 2 * a.h_kv; i += kAppendThreads)
