@@ -43,7 +43,8 @@ gqa_status fail(gqa_status s, const char* fmt, ...) {
 
 constexpr int kMaxChunkIndirect = 4096;
 constexpr size_t kMaxLdsPerWorkgroup = 160 * 1024;  // gfx950: 160 KiB of LDS per CU and workgroup
-constexpr int kMaxRows = 64;
+constexpr int kMaxRows = 512;
+constexpr int kMaxSq = 64;
 constexpr int kMaxValuRows = 8;
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -83,12 +84,14 @@ gqa_status check_shape(const gqa_decode_params* p) {
   if (p->h_q <= 0 || p->h_kv <= 0 || p->h_kv > 65535)
     return fail(GQA_ERR_INVALID_ARG, "h_q %d / h_kv %d must be positive (h_kv <= 65535)", p->h_q, p->h_kv);
   if (p->h_q % p->h_kv != 0) return fail(GQA_ERR_INVALID_ARG, "h_q %d is not a multiple of h_kv %d", p->h_q, p->h_kv);
-  if (p->s_q < 1 || p->s_q > 8) return fail(GQA_ERR_UNSUPPORTED, "s_q %d outside [1, 8]", p->s_q);
+  if (p->s_q < 1 || p->s_q > kMaxSq) return fail(GQA_ERR_UNSUPPORTED, "s_q %d outside [1, %d]", p->s_q, kMaxSq);
   if (p->head_dim != 64 && p->head_dim != 128 && p->head_dim != 256)
     return fail(GQA_ERR_UNSUPPORTED, "head_dim %d is not 64, 128 or 256", p->head_dim);
   const int64_t rows = (int64_t)(p->h_q / p->h_kv) * p->s_q;
   if (rows > kMaxRows)
     return fail(GQA_ERR_UNSUPPORTED, "(h_q/h_kv)*s_q = %lld query rows per KV head exceeds %d", (long long)rows, kMaxRows);
+  if (rows > 64 && p->kv_dtype == GQA_KV_FP8_E4M3FN && p->head_dim == 64 && p->h_kv % 2 != 0)
+    return fail(GQA_ERR_UNSUPPORTED, "more than 64 rows per KV head with FP8 d = 64 needs an even h_kv");
   if (p->layout < GQA_LAYOUT_CONTIGUOUS || p->layout > GQA_LAYOUT_PAGED)
     return fail(GQA_ERR_INVALID_ARG, "unknown layout %d", p->layout);
   if (p->kv_dtype != GQA_KV_BF16 && p->kv_dtype != GQA_KV_FP8_E4M3FN)
@@ -157,21 +160,51 @@ size_t partial_o_bytes(const gqa_decode_params* p, const gqa_decode_plan& plan) 
 // the VALU path is as fast or up to 1 % faster.
 int auto_math(int rows, int head_dim) { return rows == 1 && head_dim <= 128 ? GQA_MATH_VALU : GQA_MATH_MFMA; }
 
-// Waves per head that split the rows (2) rather than the tiles (1).  Two
-// 16-row MFMA blocks of d = 256 (17 to 32 rows) do not fit one wave's
-// registers; instead each of a head's two waves computes one block over
-// every tile, and the two share the tiles' loads through LDS.  Needs an
-// even H_kv: a workgroup then covers kPWaves / 2 heads.
-int row_share(const gqa_decode_params* p, const gqa_decode_plan& plan) {
-  return p->head_dim == 256 && plan.math == GQA_MATH_MFMA && plan.row_blocks == 2 &&
-                 p->h_kv % (gqa::kPWaves / 2) == 0
-             ? 2
-             : 1;
-}
+// How a KV head's query rows are laid over waves and workgroups.
+struct Tiling {
+  int mb = 1;          // 16-row MFMA blocks per wave (VALU: unused)
+  int share = 1;       // waves of a head that split the rows (1: they split the tiles)
+  int hpw = 1;         // KV heads per workgroup
+  int row_groups = 1;  // workgroups along the rows, each share * mb * 16 rows
+};
+static_assert(gqa::kPWaves == 4, "row sharing is laid out for 4 waves per workgroup");
 
-// KV heads per partial workgroup for this plan.
-int plan_hpw(const gqa_decode_params* p, const gqa_decode_plan& plan) {
-  return row_share(p, plan) == 2 ? gqa::kPWaves / 2 : heads_per_wg(p->h_kv);
+// Up to 16 rows: one block per wave, the waves of a head taking alternate
+// tiles.  17-32 rows: two blocks per wave, except d = 256 (two blocks of
+// d = 256 do not fit a wave's registers), where a head's two waves split
+// the rows and share the tiles through LDS (even H_kv).  More than 32 rows:
+// a head's four waves split the rows, one block each up to 64 rows, two
+// (d <= 128) beyond, and groups of more rows than one workgroup covers
+// take several row groups.  FP8 d = 64 tiles are two loads per tensor, so
+// there two waves per head split the rows, two blocks each.
+Tiling plan_tiling(const gqa_decode_params* p, int rows, int math) {
+  Tiling t;
+  t.hpw = heads_per_wg(p->h_kv);
+  if (math == GQA_MATH_VALU || rows <= 16) return t;
+  if (rows <= 32) {
+    if (p->head_dim == 256 && p->h_kv % 2 == 0) {
+      t.share = 2;
+      t.hpw = 2;
+    } else {
+      t.mb = 2;
+    }
+    return t;
+  }
+  const int loads = p->head_dim * (p->kv_dtype == GQA_KV_FP8_E4M3FN ? 1 : 2) / 32;  // per tile and tensor
+  if (loads % 4 == 0) {
+    t.share = 4;
+    t.hpw = 1;
+    t.mb = (rows > 64 && p->head_dim <= 128) ? 2 : 1;
+    t.row_groups = (int)cdiv(rows, 64 * t.mb);
+  } else if (p->h_kv % 2 == 0) {
+    t.share = 2;
+    t.hpw = 2;
+    t.mb = 2;
+    t.row_groups = (int)cdiv(rows, 64);
+  } else {
+    t.mb = 4;  // rows <= 64 (check_shape)
+  }
+  return t;
 }
 
 gqa_status make_plan(const gqa_decode_params* p, gqa_decode_plan* plan) {
@@ -181,16 +214,18 @@ gqa_status make_plan(const gqa_decode_params* p, gqa_decode_plan* plan) {
   const int rows = (p->h_q / p->h_kv) * p->s_q;
   plan->rows = rows;
   plan->math = p->math == GQA_MATH_AUTO ? auto_math(rows, p->head_dim) : p->math;
+  const Tiling tl = plan_tiling(p, rows, plan->math);
   if (plan->math == GQA_MATH_VALU)
     plan->row_blocks = rows <= 2 ? rows : (rows <= 4 ? 4 : 8);
   else
-    plan->row_blocks = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
+    plan->row_blocks = tl.mb * tl.share * tl.row_groups;
   const bool indirect = p->layout == GQA_LAYOUT_PAGED || p->topk > 0;
   const bool packed = packed_mode(p);
   const int64_t L = p->topk > 0 ? p->topk : p->max_seqlen_kv;
   const int64_t pairs = (int64_t)p->batch * p->h_kv;
-  const int hpw = plan_hpw(p, *plan);
-  const int64_t groups = p->h_kv / hpw;
+  const int hpw = tl.hpw;
+  const int64_t groups = (int64_t)(p->h_kv / hpw) * tl.row_groups;  // grid.y: head groups x row groups
+  if (groups > 65535) return fail(GQA_ERR_UNSUPPORTED, "h_kv %d with %d row groups exceeds the grid", p->h_kv, tl.row_groups);
   int64_t chunk = p->kv_chunk;
   if (chunk == 0) {
     int cus = p->num_cus ? p->num_cus : device_cus();
@@ -200,12 +235,12 @@ gqa_status make_plan(const gqa_decode_params* p, gqa_decode_plan* plan) {
       const int64_t per = cdiv(p->kv_rows * groups, cus);
       chunk = std::min<int64_t>(round_up(std::max<int64_t>(per, 64), 32), 1 << 24);
     } else {
-      // A workgroup covers hpw heads x chunk list positions.  Aim for about
+      // A workgroup covers hpw heads x chunk list positions (x one row group).  Aim for about
       // one workgroup per CU over the whole grid (MI355X measurements: one
       // resident round of long workgroups streams best and writes the
       // fewest partials), with 128..4096 positions per workgroup and never
       // more than the list.
-      const int64_t per = cdiv(std::max<int64_t>(pairs * L, 1), (int64_t)cus * hpw);
+      const int64_t per = cdiv(std::max<int64_t>(pairs * L * tl.row_groups, 1), (int64_t)cus * hpw);
       chunk = round_up(std::max<int64_t>(per, 128), 128);
       chunk = std::min<int64_t>(chunk, 4096);
       chunk = std::min<int64_t>(chunk, round_up(std::max<int64_t>(L, 1), 32));
@@ -287,7 +322,7 @@ void fill_args(gqa::DecodeArgs& a, const gqa_decode_params* p, const gqa_decode_
   a.gate_mode = p->gate_mode;
   a.chunk = plan.kv_chunk;
   a.num_splits = plan.num_splits;
-  a.heads_per_wg = plan_hpw(p, plan);
+  a.heads_per_wg = plan_tiling(p, plan.rows, plan.math).hpw;
   a.packed = packed_mode(p) ? 1 : 0;
   if (a.packed) {
     a.part_sb = (int64_t)p->h_kv * plan.rows;
@@ -438,10 +473,11 @@ gqa_status gqa_decode_run(const gqa_decode_params* p, const void* q, const void*
   const bool indirect = p->layout == GQA_LAYOUT_PAGED || p->topk > 0;
   const int mode = a.packed ? 2 : (indirect ? 1 : 0);
   // Packed chunks span requests: one grid row covers the whole batch.
-  const dim3 grid(plan.num_splits, p->h_kv / a.heads_per_wg, a.packed ? 1 : p->batch);
+  const Tiling tl = plan_tiling(p, plan.rows, plan.math);
+  const dim3 grid(plan.num_splits, (p->h_kv / tl.hpw) * tl.row_groups, a.packed ? 1 : p->batch);
   const bool valu = plan.math == GQA_MATH_VALU;
-  hipError_t e = gqa::launch_partial(a, p->head_dim, p->kv_dtype == GQA_KV_FP8_E4M3FN, mode, valu ? 1 : plan.row_blocks,
-                                     valu ? plan.row_blocks : 0, row_share(p, plan), grid, s,
+  hipError_t e = gqa::launch_partial(a, p->head_dim, p->kv_dtype == GQA_KV_FP8_E4M3FN, mode, valu ? 1 : tl.mb,
+                                     valu ? plan.row_blocks : 0, tl.share, grid, s,
                                      static_cast<hipEvent_t>(p->partial_event_begin),
                                      static_cast<hipEvent_t>(p->partial_event_end));
   if (e != hipSuccess) return hip_fail(e, "partial kernel launch");

@@ -125,21 +125,28 @@ constexpr int partial_min_blocks() { return (MB == 1 && (FP8 || D == 64) && RV =
 //       lanes of the token completes the score in all of them.
 //   PV: the lane accumulates p x V over its own token slot for its ELT
 //       columns; the token slots are summed once, after the last tile.
-// SHARE = 2 (d = 256, 17 to 32 query rows): the two waves of a head split
-// the rows instead of the tiles.  Each computes one 16-row block over every
-// tile of the chunk, and each loads and stages half of every tile into a
+// SHARE = 2 or 4 (row sharing): the SHARE waves of a head split the rows
+// instead of the tiles.  Each computes MB 16-row blocks over every tile of
+// the chunk, and each loads and stages 1/SHARE of every tile into a
 // head-wide, double-buffered LDS tile (an LDS-only barrier per tile).  HBM
-// still reads each tile once, and a wave's registers are those of the
-// one-block kernel: two row blocks of d = 256 in one wave do not fit.
+// still reads each tile once per workgroup, and a wave's registers are
+// those of a one- or two-block kernel.  Used for d = 256 with 17 to 32 rows
+// (two blocks of d = 256 in one wave do not fit) and for every group of
+// more than 32 rows; a workgroup covers SHARE * MB * 16 rows (row group
+// blockIdx.y / (H_kv / HPW)), and a group of up to 512 rows takes several
+// row groups, each reading the chunk.
 template <int D, bool FP8, int MODE, int MB, int RV, int SHARE>
 __global__ void __launch_bounds__(kPThreads, (partial_min_blocks<D, FP8, MB, RV, SHARE>()))
     gqa_partial_kernel(DecodeArgs a) {
   using TS = TileShape<D, FP8>;
   constexpr int RB = TS::RB, CPR = TS::CPR, TPI = TS::TPI, NLD = TS::NLD, KK = TS::KK, NB = TS::NB;
-  constexpr int NPART = TS::NPART, NLDP = TS::NLDP;
-  static_assert(RV == 0 || D <= 128, "the VALU variant is built for d <= 128");
-  static_assert(SHARE == 1 || (SHARE == 2 && D == 256 && MB == 1 && RV == 0), "row sharing: d = 256, one block per wave");
   constexpr bool SHARED = SHARE > 1;
+  constexpr int NPART = TS::NPART;
+  // Loads per part: a shared tile is loaded in SHARE parts, one per wave.
+  constexpr int NLDP = NLD / (SHARED ? SHARE : NPART);
+  static_assert(RV == 0 || D <= 128, "the VALU variant is built for d <= 128");
+  static_assert(SHARE == 1 || ((SHARE == 2 || SHARE == 4) && RV == 0 && MB <= 2 && NLD % SHARE == 0),
+                "row sharing: 2 or 4 waves per head, one or two blocks per wave");
   constexpr bool INDIRECT = MODE == kIndirect;
   constexpr bool PACKED = MODE == kPacked;
   constexpr bool VALU = RV > 0;
@@ -162,8 +169,10 @@ __global__ void __launch_bounds__(kPThreads, (partial_min_blocks<D, FP8, MB, RV,
   const int wph = kPWaves / hpw;                 // waves per head
   const int hs = wave % hpw;                    // head slot of this wave
   const int sub = wave / hpw;                   // this wave's share of the head's tiles (or rows)
-  const int rbase = SHARED ? 16 * sub : 0;      // first query row of this wave's blocks
-  const int g0 = blockIdx.y * hpw;
+  const int hgroups = a.h_kv / hpw;             // head groups in grid.y (times the row groups)
+  const int rgroup = blockIdx.y / hgroups;
+  const int rbase = SHARED ? (rgroup * SHARE + sub) * MB * 16 : 0;  // first query row of this wave's blocks
+  const int g0 = (blockIdx.y - rgroup * hgroups) * hpw;
   const int g = g0 + hs;
   const int split = blockIdx.x;
 
@@ -600,12 +609,12 @@ __global__ void __launch_bounds__(kPThreads, (partial_min_blocks<D, FP8, MB, RV,
   // (an exit between the two steps gives the loop a path on which A's
   // loads are the youngest, and every pass then waits for all loads).
   if constexpr (SHARED) {
-    // Rows shared by the two waves of a head: both walk every tile of the
-    // chunk; wave `sub` loads and stages half `sub` of each tile into the
+    // Rows shared by the SHARE waves of a head: all walk every tile of the
+    // chunk; wave `sub` loads and stages part `sub` of each tile into the
     // head's LDS buffer of the tile's parity.  A step stages the next tile's
-    // half into the buffer the previous tile used, refills the staged
+    // part into the buffer the previous tile used, refills the staged
     // registers with the tile two beyond it, and computes the current tile;
-    // the LDS-only barrier that ends the step makes the staged halves
+    // the LDS-only barrier that ends the step makes the staged parts
     // visible and frees the computed buffer, while both register buffers
     // stay in flight.  Two tiles per pass, one exit test, and a tail for an
     // odd last tile.
@@ -733,12 +742,14 @@ __global__ void __launch_bounds__(kPThreads, (partial_min_blocks<D, FP8, MB, RV,
   }
 
   if constexpr (SHARED) {
-    // Each wave holds complete rows (16 of its head's group): normalise and
-    // write them from registers.  Lane (m16, qd) has row rbase + m16,
-    // columns 16 nb + 4 qd .. +3.
-    const int r = rbase + m16;
-    if (r < a.rows) {
-      const float m = mrun[0], l = lrun[0];
+    // Each wave holds complete rows (MB blocks of 16 of its head's group):
+    // normalise and write them from registers.  Lane (m16, qd) of block mb
+    // has row rbase + 16 mb + m16, columns 16 nb + 4 qd .. +3.
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int r = rbase + mb * 16 + m16;
+      if (r >= a.rows) continue;
+      const float m = mrun[mb], l = lrun[mb];
       const bool empty = (m == -INFINITY);
       const float inv = empty ? 0.f : (FP8 ? a.v_scale[b * a.h_kv + g] : 1.f) / l;
       const float lse2 = empty ? -INFINITY : m + __log2f(l);
@@ -759,7 +770,7 @@ __global__ void __launch_bounds__(kPThreads, (partial_min_blocks<D, FP8, MB, RV,
           const int col = 16 * nb + 4 * qd;
           float o[4];
 #pragma unroll
-          for (int c = 0; c < 4; ++c) o[c] = acc[0][nb][c] * inv * sgh;
+          for (int c = 0; c < 4; ++c) o[c] = acc[mb][nb][c] * inv * sgh;
           if (egate) {
             o[0] *= sigmoidf_(bf16_lo(gw[nb].x));
             o[1] *= sigmoidf_(bf16_hi(gw[nb].x));
@@ -773,7 +784,7 @@ __global__ void __launch_bounds__(kPThreads, (partial_min_blocks<D, FP8, MB, RV,
         const int64_t prow = b * a.part_sb + g * a.part_sg + split * a.part_ss + r;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
-          *reinterpret_cast<f32x4*>(a.o_part + prow * D + 16 * nb + 4 * qd) = acc[0][nb] * inv;
+          *reinterpret_cast<f32x4*>(a.o_part + prow * D + 16 * nb + 4 * qd) = acc[mb][nb] * inv;
         if (qd == 0) a.lse_part[prow] = lse2;
       }
     }
@@ -1060,8 +1071,20 @@ static hipError_t launch_partial_t(const DecodeArgs& a, dim3 grid, hipStream_t s
 template <int D, bool FP8, int MODE>
 static hipError_t launch_mb(const DecodeArgs& a, int mb, int rv, int share, dim3 grid, hipStream_t st,
                             hipEvent_t ev0, hipEvent_t ev1) {
-  if constexpr (D == 256) {
-    if (share == 2) return launch_partial_t<D, FP8, MODE, 1, 0, 2>(a, grid, st, ev0, ev1);
+  // Row sharing: the combinations the planner picks (share_tiling in the
+  // host code) and no others.
+  constexpr int NLD = TileShape<D, FP8>::NLD;
+  if (share == 2) {
+    if constexpr (D == 256) return launch_partial_t<D, FP8, MODE, 1, 0, 2>(a, grid, st, ev0, ev1);
+    if constexpr (NLD == 2) return launch_partial_t<D, FP8, MODE, 2, 0, 2>(a, grid, st, ev0, ev1);
+    return hipErrorInvalidValue;
+  }
+  if (share == 4) {
+    if constexpr (NLD % 4 == 0) {
+      if (mb == 1) return launch_partial_t<D, FP8, MODE, 1, 0, 4>(a, grid, st, ev0, ev1);
+      if constexpr (D <= 128) return launch_partial_t<D, FP8, MODE, 2, 0, 4>(a, grid, st, ev0, ev1);
+    }
+    return hipErrorInvalidValue;
   }
   if constexpr (D <= 128) {
     if (rv > 0) {

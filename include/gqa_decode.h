@@ -77,7 +77,7 @@ enum { GQA_GATE_NONE = 0, GQA_GATE_ELEMENTWISE = 1, GQA_GATE_HEADWISE = 2 };
 /* Arithmetic of the two products (scores and P.V).  Both run on the same K/V
  * loads and LDS staging; they differ only in the units that multiply:
  *   GQA_MATH_MFMA  v_mfma_f32_16x16x32_bf16 on 16-row blocks of query rows
- *                  (the rows of a KV head's group padded to 16, 32 or 64);
+ *                  (the rows of a KV head's group padded to a multiple of 16);
  *   GQA_MATH_VALU  v_dot2_f32_bf16 and fp32 FMAs on exactly the group's rows,
  *                  for at most 8 query rows per KV head;
  *   GQA_MATH_AUTO  the faster one for the row count, as measured on MI355X:
@@ -91,9 +91,9 @@ enum { GQA_MATH_AUTO = 0, GQA_MATH_MFMA = 1, GQA_MATH_VALU = 2 };
 
 typedef struct gqa_decode_params {
   int32_t batch;             /* B >= 0                                                  */
-  int32_t s_q;               /* query tokens per request, 1..8                          */
+  int32_t s_q;               /* query tokens per request, 1..64                         */
   int32_t h_q;               /* query heads                                             */
-  int32_t h_kv;              /* KV heads; h_q % h_kv == 0, (h_q/h_kv)*s_q <= 64         */
+  int32_t h_kv;              /* KV heads; h_q % h_kv == 0, (h_q/h_kv)*s_q <= 512        */
   int32_t head_dim;          /* 64, 128 or 256 (the VALU path: 64 or 128)              */
   int32_t layout;            /* GQA_LAYOUT_*                                            */
   int32_t kv_dtype;          /* GQA_KV_*                                                */
@@ -122,8 +122,9 @@ typedef struct gqa_decode_params {
 
 typedef struct gqa_decode_plan {
   int32_t rows;              /* query rows sharing one KV head: (h_q / h_kv) * s_q      */
-  int32_t row_blocks;        /* MFMA: 16-row blocks computed (1, 2, 4); VALU: rows
-                                computed (1, 2, 4 or 8, at least the group's rows)      */
+  int32_t row_blocks;        /* MFMA: 16-row blocks computed per KV head (the group's
+                                rows padded to the tiling); VALU: rows computed (1, 2,
+                                4 or 8, at least the group's rows)                      */
   int32_t kv_chunk;          /* list positions per workgroup                            */
   int32_t num_splits;        /* workgroups per (request, KV head) for the longest list  */
   int64_t partial_workgroups;/* grid size of the partial kernel                         */

@@ -63,12 +63,13 @@ BAD_SHAPES = [
     (dict(h_q=6, h_kv=4), 1),
     (dict(h_kv=0), 1),
     (dict(s_q=0), 2),
-    (dict(s_q=9), 2),
+    (dict(s_q=65), 2),
     (dict(head_dim=96), 2),
     (dict(head_dim=512), 2),
     (dict(head_dim=256, math="valu"), 2),         # the VALU path is built for d <= 128
-    (dict(h_q=128, h_kv=1), 2),             # 128 rows per KV head
-    (dict(h_q=16, h_kv=1, s_q=8), 2),       # 128 rows
+    (dict(h_q=1024, h_kv=1), 2),            # 1024 rows per KV head
+    (dict(h_q=16, h_kv=1, s_q=64), 2),      # 1024 rows
+    (dict(h_q=80, h_kv=1, kv_dtype="fp8_e4m3fn", head_dim=64), 2),   # FP8 d64, > 64 rows, odd H_kv
     (dict(layout=7), 1),
     (dict(kv_dtype=3), 1),
     (dict(gate_mode=5), 1),
@@ -235,3 +236,20 @@ def test_append_workspace_only_for_multi_block_first_block():
 
 def test_append_batch_zero_is_a_no_op():
     assert _append(append_base(batch=0)) == 0
+
+
+def test_plan_tiling_of_large_groups():
+    # rows -> 16-row blocks per KV head: up to 64 rows one block per wave of
+    # four; beyond, two blocks per wave (d <= 128) in row groups of 128
+    def plan(**kw):
+        d = dict(batch=1, s_q=1, h_q=8, h_kv=8, head_dim=128, max_seqlen_kv=4096, seq_capacity=4096,
+                 kv_rows=4096, num_cus=256)
+        d.update(kw)
+        return G.gqa_decode_make_plan(G.make_params(**d))
+    assert plan(h_q=48, h_kv=1)["row_blocks"] == 4                       # 48 rows: 4 waves x 1 block
+    assert plan(h_q=64, h_kv=8, s_q=16)["row_blocks"] == 8               # 128 rows: 4 x 2
+    assert plan(h_q=64, h_kv=8, s_q=64)["row_blocks"] == 32              # 512 rows: 4 row groups of 128
+    assert plan(h_q=64, h_kv=8, s_q=64, head_dim=256)["row_blocks"] == 32  # d256: 8 groups of 64
+    assert plan(h_q=32, h_kv=2, s_q=2, head_dim=256)["row_blocks"] == 2  # two waves x 1 block
+    p1, p4 = plan(h_q=64, h_kv=8, s_q=2), plan(h_q=64, h_kv=8, s_q=64)
+    assert p4["partial_workgroups"] >= p1["partial_workgroups"]
