@@ -42,6 +42,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "µs/call and achieved HBM GB/s (% of peak), GQA decode 64/8 d128 128K KV"
 HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix peak of MI355X
 KERNEL_SOURCES = ["gqa_kv_cache_amd/csrc/gqa_kernels.hip", "gqa_kv_cache_amd/csrc/gqa_device.h"]
 
 
@@ -159,7 +160,7 @@ def main():
     ap.add_argument("--workload", default=None,
                     choices=["tiny", "long128k", "ragged", "ragged_sq8", "paged", "sparse_fp8",
                              "long_32x8", "long_8x1", "long_64x8_d64", "long_32x2_d256",
-                             "append_decode", "append_prefill"])
+                             "ragged_sq16", "long_sq64", "append_decode", "append_prefill"])
     ap.add_argument("--scale-policy", default=None, choices=["given", "first_block"],
                     help="append: scale policy (default: the workload's)")
     ap.add_argument("--kv-chunk", type=int, default=0, help="force list positions per workgroup")
@@ -318,6 +319,24 @@ def main():
         extra["d2d_copy_512MiB_GBps"] = calibrate_copy(torch, stream)
 
     traffic = read_traffic(args.workload)
+    # The partial kernel's binding roofline: HBM, unless its matrix work per
+    # K/V byte exceeds the ridge (peak FLOP/s over peak bytes/s), as for
+    # query blocks of hundreds of rows per KV head.
+    from gqa_kv_cache_amd import costs
+    flops = costs.decode_flops(tokens=tokens, h_q=s.h_q, d=s.head_dim, s_q=s.s_q)
+    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
+    if flops / kv_bytes > ridge:
+        tflops = flops / (partial_us * 1e-6) / 1e12
+        roofline = {"bound": "mfma", "kernel": "gqa_partial_kernel", "achieved": round(tflops, 2),
+                    "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                    "traffic": None if traffic is None else int(traffic), "algorithmic_flops_per_launch": flops,
+                    "algorithmic_bytes_per_launch": kv_bytes, "kv_GBps": round(achieved, 2),
+                    "kernel_us": round(partial_us, 3)}
+    else:
+        roofline = {"bound": "hbm", "kernel": "gqa_partial_kernel", "achieved": round(achieved, 2),
+                    "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                    "traffic": None if traffic is None else int(traffic), "algorithmic_bytes_per_launch": kv_bytes,
+                    "kernel_us": round(partial_us, 3)}
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -341,17 +360,7 @@ def main():
         "us_per_call": round(us_per_call, 3),
         "min_bytes_per_call": min_bytes,
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
-        "roofline": {
-            "bound": "hbm",
-            "kernel": "gqa_partial_kernel",
-            "achieved": round(achieved, 2),
-            "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": None if traffic is None else int(traffic),
-            "algorithmic_bytes_per_launch": kv_bytes,
-            "kernel_us": round(partial_us, 3),
-        },
+        "roofline": roofline,
         **extra,
     }
     ok = True

@@ -290,6 +290,13 @@ LONG_64X8_D64 = Spec(name="long_64x8_d64_sq2_128k", batch=1, h_q=64, h_kv=8, hea
                      s_q=2, seqlen=131072, causal=True)
 LONG_32X2_D256 = Spec(name="long_32x2_d256_sq2_128k", batch=1, h_q=32, h_kv=2, head_dim=256,
                       s_q=2, seqlen=131072, causal=True)
+# Multi-token query blocks: speculative verification of 16 draft tokens
+# over the ragged S_q 8 batch's caches, and a 64-token prefill chunk
+# against a 128K-token cache (512 query rows per KV head).
+RAGGED_B32_SQ16 = Spec(name="ragged_b32_32x8_d128_sq16_8k", batch=32, h_q=32, h_kv=8,
+                       head_dim=128, s_q=16, seqlen=8192, layout=LAYOUT_RAGGED, causal=True)
+LONG_SQ64 = Spec(name="long_64x8_d128_sq64_128k", batch=1, h_q=64, h_kv=8, head_dim=128,
+                 s_q=64, seqlen=131072, causal=True)
 
 NAMED = {
     "tiny": (TINY, 1),
@@ -302,6 +309,8 @@ NAMED = {
     "long_8x1": (LONG_8X1, 7),
     "long_64x8_d64": (LONG_64X8_D64, 8),
     "long_32x2_d256": (LONG_32X2_D256, 9),
+    "ragged_sq16": (RAGGED_B32_SQ16, 34),
+    "long_sq64": (LONG_SQ64, 35),
 }
 
 

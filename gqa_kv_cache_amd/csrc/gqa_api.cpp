@@ -224,6 +224,15 @@ gqa_status make_plan(const gqa_decode_params* p, gqa_decode_plan* plan) {
   const int64_t L = p->topk > 0 ? p->topk : p->max_seqlen_kv;
   const int64_t pairs = (int64_t)p->batch * p->h_kv;
   const int hpw = tl.hpw;
+  // Resident workgroups per CU the grid is sized for.  Measured on MI355X
+  // (one process, both plans): the row-sharing variants that fit two per CU
+  // run faster with two (32 x 8192 tokens at S_q 16: 229 -> 202 us packed,
+  // 192 -> 185 us contiguous); the tile-splitting ones that fit two run
+  // faster with one long round (d = 64: 50.2 against 53.0 us; FP8 d = 128:
+  // 51.4 against 53.0 us at 128K tokens).
+  const int occ = plan->math == GQA_MATH_MFMA && tl.share > 1
+                      ? gqa::partial_wgs_per_cu(p->head_dim, p->kv_dtype == GQA_KV_FP8_E4M3FN, tl.mb, 0, tl.share)
+                      : 1;
   const int64_t groups = (int64_t)(p->h_kv / hpw) * tl.row_groups;  // grid.y: head groups x row groups
   if (groups > 65535) return fail(GQA_ERR_UNSUPPORTED, "h_kv %d with %d row groups exceeds the grid", p->h_kv, tl.row_groups);
   int64_t chunk = p->kv_chunk;
@@ -231,16 +240,16 @@ gqa_status make_plan(const gqa_decode_params* p, gqa_decode_plan* plan) {
     int cus = p->num_cus ? p->num_cus : device_cus();
     if (cus <= 0) return fail(GQA_ERR_HIP, "cannot query the device's compute-unit count");
     if (packed) {
-      // One workgroup per CU over the packed rows, each the same size.
-      const int64_t per = cdiv(p->kv_rows * groups, cus);
+      // One round of resident workgroups over the packed rows, each the same size.
+      const int64_t per = cdiv(p->kv_rows * groups, (int64_t)cus * occ);
       chunk = std::min<int64_t>(round_up(std::max<int64_t>(per, 64), 32), 1 << 24);
     } else {
-      // A workgroup covers hpw heads x chunk list positions (x one row group).  Aim for about
-      // one workgroup per CU over the whole grid (MI355X measurements: one
-      // resident round of long workgroups streams best and writes the
-      // fewest partials), with 128..4096 positions per workgroup and never
-      // more than the list.
-      const int64_t per = cdiv(std::max<int64_t>(pairs * L * tl.row_groups, 1), (int64_t)cus * hpw);
+      // A workgroup covers hpw heads x chunk list positions (x one row
+      // group).  Aim for one resident round of workgroups over the whole
+      // grid -- occ per CU (MI355X measurements: one resident round of long
+      // workgroups streams best and writes the fewest partials), with
+      // 128..4096 positions per workgroup and never more than the list.
+      const int64_t per = cdiv(std::max<int64_t>(pairs * L * tl.row_groups, 1), (int64_t)cus * occ * hpw);
       chunk = round_up(std::max<int64_t>(per, 128), 128);
       chunk = std::min<int64_t>(chunk, 4096);
       chunk = std::min<int64_t>(chunk, round_up(std::max<int64_t>(L, 1), 32));

@@ -30,6 +30,19 @@ constexpr int kTile = 32;       // list positions per wave iteration
 #define GQA_PARTIAL_WAVES 4
 #endif
 constexpr int kPWaves = GQA_PARTIAL_WAVES;
+
+// Resident partial workgroups per CU that a kernel variant's register
+// budget is built for (its launch bounds), and that the planner sizes the
+// grid for.  Two for one 16-row block of FP8 or d = 64 tiles, and for the
+// row-sharing variants with one block per wave at d <= 128; one (the whole
+// register file) for bf16 d = 128 with the waves splitting the tiles, whose
+// two register buffers of whole-row loads alone take 128 VGPRs -- squeezed
+// into half the file it spills, and every spill reload waits for all loads
+// in flight.  The VALU variant keeps RV x (8 or 16) fp32 accumulators and
+// every score of a tile per lane, and also takes the whole file.
+__host__ __device__ constexpr int partial_wgs_per_cu(int D, bool fp8, int mb, int rv, int share) {
+  return (rv == 0 && mb == 1 && ((share == 1 && (fp8 || D == 64)) || (share == 4 && D <= 128))) ? 2 : 1;
+}
 constexpr int kPThreads = 64 * kPWaves;
 
 // Everything a kernel needs, passed by value (kernarg segment).

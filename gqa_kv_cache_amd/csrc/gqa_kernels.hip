@@ -107,15 +107,8 @@ __device__ __forceinline__ int vblk(int blk, int tok) {
 //             number of rows, however the lengths vary.
 constexpr int kDense = 0, kIndirect = 1, kPacked = 2;
 
-// Resident workgroups per CU the register budget is sized for: two for one
-// 16-row block of FP8 or d = 64 tiles; one (the whole register file) for
-// bf16 d = 128, whose two register buffers of whole-row loads alone take
-// 128 VGPRs -- squeezed into half the file it spills, and every spill
-// reload waits for all loads in flight.
-// The VALU variant keeps RV x (8 or 16) fp32 accumulators and every score
-// of a tile per lane, and also takes the whole file.
 template <int D, bool FP8, int MB, int RV, int SHARE>
-constexpr int partial_min_blocks() { return (MB == 1 && (FP8 || D == 64) && RV == 0 && SHARE == 1) ? 2 : 1; }
+constexpr int partial_min_blocks() { return partial_wgs_per_cu(D, FP8, MB, RV, SHARE); }
 
 // MB: 16-row MFMA blocks (RV = 0).  RV > 0 selects the VALU variant for up
 // to RV query rows (MB = 1): the same loads, LDS staging and pipeline, with
