@@ -83,7 +83,7 @@ def workload_bytes(w):
     """(minimum bytes per call, algorithmic K/V bytes per partial launch)."""
     from gqa_kv_cache_amd import costs
     s = w.spec
-    es = 1 if s.kv_dtype == "fp8_e4m3fn" else 2
+    es = 1 if s.kv_dtype in ("fp8_e4m3fn", "int8") else 2
     if s.topk:
         tokens = sum(len(set(int(t) for t in w.topk_idx[b] if 0 <= t < w.seqlens[b])) for b in range(s.batch))
     else:
@@ -93,7 +93,7 @@ def workload_bytes(w):
         pages = sum(-(-int(n) // s.page_size) for n in w.seqlens)
     mb = costs.minimum_bytes(batch=s.batch, s_q=s.s_q, h_q=s.h_q, h_kv=s.h_kv, d=s.head_dim,
                              kv_elem_bytes=es, tokens=tokens, layout=s.layout, pages_touched=pages,
-                             topk=s.topk, fp8_scales=s.kv_dtype == "fp8_e4m3fn", gate=w.gate is not None)
+                             topk=s.topk, fp8_scales=s.kv_dtype in ("fp8_e4m3fn", "int8"), gate=w.gate is not None)
     kv = 2 * tokens * s.h_kv * s.head_dim * es
     return mb, kv, tokens
 
@@ -209,7 +209,7 @@ def main():
     def bf16(x):
         return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
 
-    fp8 = s.kv_dtype == "fp8_e4m3fn"
+    fp8 = s.kv_dtype in ("fp8_e4m3fn", "int8")   # one-byte codes with scales
     q = bf16(w.q)
     k = torch.from_numpy(w.k_cache).to(dev) if fp8 else bf16(w.k_cache)
     v = torch.from_numpy(w.v_cache).to(dev) if fp8 else bf16(w.v_cache)
@@ -348,7 +348,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8_e4m3fn->bf16" if fp8 else "bf16",
+        "dtype": f"{s.kv_dtype}->bf16" if fp8 else "bf16",
         "data": "synthetic",
         "config": {
             "workload": s.name, "batch": s.batch, "h_q": s.h_q, "h_kv": s.h_kv, "head_dim": s.head_dim,

@@ -44,6 +44,8 @@ LAYOUT_PAGED = "paged"
 
 KV_BF16 = "bf16"
 KV_FP8 = "fp8_e4m3fn"
+KV_INT8 = "int8"
+INT8_MAX = 127.0
 
 E4M3FN_MAX = 448.0
 
@@ -89,6 +91,13 @@ def quantize_e4m3fn(x: np.ndarray, scale: np.ndarray) -> np.ndarray:
                 -E4M3FN_MAX, E4M3FN_MAX).astype(np.float32)
     t = torch.from_numpy(np.ascontiguousarray(y)).to(torch.float8_e4m3fn)
     return t.view(torch.uint8).numpy().copy()
+
+
+def quantize_int8(x: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """Encode float32 values x / scale as int8 codes (returned as their
+    uint8 bytes): float32 quotient, clamp to +-127, round half to even."""
+    y = np.clip(np.asarray(x, np.float32) / np.asarray(scale, np.float32), -INT8_MAX, INT8_MAX)
+    return np.rint(y).astype(np.int8).view(np.uint8)
 
 
 @dataclasses.dataclass
@@ -173,7 +182,8 @@ def build(spec: Spec, seed: int) -> Workload:
     cu = None
     bt = None
     k_scale = v_scale = None
-    fp8 = spec.kv_dtype == KV_FP8
+    fp8 = spec.kv_dtype in (KV_FP8, KV_INT8)   # one-byte codes with per-(request, head) scales
+    qmax, quant = (INT8_MAX, quantize_int8) if spec.kv_dtype == KV_INT8 else (E4M3FN_MAX, quantize_e4m3fn)
 
     if spec.layout == LAYOUT_CONTIGUOUS:
         cap = spec.capacity if spec.capacity is not None else max(int(lens.max()), 1)
@@ -227,9 +237,9 @@ def build(spec: Spec, seed: int) -> Workload:
                 else:
                     flat = blk.reshape(-1, Hkv, d)
                 amax = np.abs(flat).max(axis=(0, 2)) if n else np.zeros(Hkv, np.float32)
-                s = np.where(amax > 0, amax / np.float32(E4M3FN_MAX), np.float32(1.0)).astype(np.float32)
+                s = np.where(amax > 0, amax / np.float32(qmax), np.float32(1.0)).astype(np.float32)
                 sc[b] = s
-                dst[sel] = quantize_e4m3fn(blk, s[None, :, None] if blk.ndim == 3 else s[None, None, :, None])
+                dst[sel] = quant(blk, s[None, :, None] if blk.ndim == 3 else s[None, None, :, None])
         del kf, vf
 
     topk = None

@@ -26,7 +26,13 @@ the pages, with no blocking, fusion or reordering beyond the definition:
   kernels fold ``k_scale`` into the score scale and apply ``v_scale`` once
   at the end, which is the same quantity in exact arithmetic);
 * paging with 16-token pages addressed through a block table (same page,
-  "Workload").
+  "Workload");
+* an int8 K/V cache, dequantised inside attention rather than as a whole
+  -- "Profiling down to the register, then an extension that broke my
+  assumptions twice", int8 KV-cache section.  The page gives no encoding;
+  the reading taken is the FP8 one with the integer format: a stored code
+  (two's complement int8) means ``code * scale`` with one scale per
+  (request, KV head).
 
 Readings where the pages are silent (each is listed with its reason in the
 design notes): LSE is the natural log-sum-exp of the *scaled* scores; a
@@ -54,6 +60,7 @@ RAGGED = "ragged"
 PAGED = "paged"
 
 FP8 = "fp8_e4m3fn"
+INT8 = "int8"
 BF16 = "bf16"
 
 
@@ -88,6 +95,13 @@ def e4m3fn_table() -> np.ndarray:
 
 
 _E4M3FN = None
+
+
+def int8_codes_to_f64(codes: np.ndarray) -> np.ndarray:
+    """Two's complement bytes: 0x00..0x7F are 0..127, 0x80..0xFF are
+    -128..-1.  Exact."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    return np.where(c >= 128, c - 256, c).astype(np.float64)
 
 
 def fp8_codes_to_f64(codes: np.ndarray) -> np.ndarray:
@@ -198,8 +212,8 @@ def reference_decode(*, q, k_cache, v_cache, h_q: int, h_kv: int, head_dim: int,
                      rows: Optional[Iterable[Tuple[int, int, int]]] = None):
     """fp64 reference for one decode call.
 
-    q: bf16 bits [B, S_q, H_q, d].  k_cache / v_cache: bf16 bits or FP8 codes
-    in the layout named by ``layout``.  Returns (O [B, S_q, H_q, d] float64,
+    q: bf16 bits [B, S_q, H_q, d].  k_cache / v_cache: bf16 bits, or FP8 or
+    int8 codes, in the layout named by ``layout``.  Returns (O [B, S_q, H_q, d] float64,
     LSE [B, H_q, S_q] float64).  ``rows`` restricts the work to a list of
     (b, i, h); other entries are left NaN."""
     B = q.shape[0]
@@ -208,6 +222,7 @@ def reference_decode(*, q, k_cache, v_cache, h_q: int, h_kv: int, head_dim: int,
     assert h_q % h_kv == 0
     scale = (1.0 / math.sqrt(d)) if not softmax_scale else float(softmax_scale)
     fp8 = kv_dtype == FP8
+    int8 = kv_dtype == INT8
     capacity = k_cache.shape[1] if layout == CONTIGUOUS else 0
     # flatten the token axes: row-major [rows, H_kv, d]
     kf = k_cache.reshape(-1, h_kv, d)
@@ -228,6 +243,9 @@ def reference_decode(*, q, k_cache, v_cache, h_q: int, h_kv: int, head_dim: int,
         if fp8:
             Kh = fp8_codes_to_f64(kf[idx, g, :]) * float(k_scale[b, g])
             Vh = fp8_codes_to_f64(vf[idx, g, :]) * float(v_scale[b, g])
+        elif int8:
+            Kh = int8_codes_to_f64(kf[idx, g, :]) * float(k_scale[b, g])
+            Vh = int8_codes_to_f64(vf[idx, g, :]) * float(v_scale[b, g])
         else:
             Kh = bf16_bits_to_f64(kf[idx, g, :])
             Vh = bf16_bits_to_f64(vf[idx, g, :])

@@ -32,6 +32,11 @@ def _decode_fp8(codes: np.ndarray) -> np.ndarray:
     return t.to(torch.float64).numpy()
 
 
+def _decode_int8(codes: np.ndarray) -> np.ndarray:
+    t = torch.from_numpy(np.ascontiguousarray(codes)).view(torch.int8)
+    return t.to(torch.float64).numpy()
+
+
 def _inverse_rows(w):
     """Map every physical token row to (request, logical token) or None."""
     s = w.spec
@@ -68,7 +73,7 @@ def brute_decode(w, softmax_scale=None):
     scale = softmax_scale if softmax_scale else 1.0 / math.sqrt(d)
     groups = np.array_split(np.arange(Hq), Hkv)
     head_of = {int(h): gi for gi, grp in enumerate(groups) for h in grp}
-    dec = _decode_fp8 if s.kv_dtype == "fp8_e4m3fn" else _decode_bf16
+    dec = {"fp8_e4m3fn": _decode_fp8, "int8": _decode_int8}.get(s.kv_dtype, _decode_bf16)
     K = dec(w.k_cache).reshape(-1, Hkv, d)
     V = dec(w.v_cache).reshape(-1, Hkv, d)
     q = _decode_bf16(w.q)

@@ -47,7 +47,7 @@ class Uploaded:
                  device="cuda"):
         s = w.spec
         self.w = w
-        fp8 = s.kv_dtype == gi.KV_FP8
+        fp8 = s.kv_dtype in (gi.KV_FP8, gi.KV_INT8)   # one-byte codes
         self.q = bf16_tensor(w.q, device)
         if fp8:
             self.k = torch.from_numpy(np.ascontiguousarray(w.k_cache)).to(device)
@@ -142,4 +142,4 @@ def check_workload(w: gi.Workload, *, kv_chunk=0, gate_mode=None, softmax_scale=
     up.run()
     O, LSE = up.result()
     Oref, Lref = oracle(w, gate_mode=up.gate_mode, softmax_scale=softmax_scale)
-    return compare(O, LSE, Oref, Lref, fp8=w.spec.kv_dtype == gi.KV_FP8, label=label or w.spec.name)
+    return compare(O, LSE, Oref, Lref, fp8=w.spec.kv_dtype in (gi.KV_FP8, gi.KV_INT8), label=label or w.spec.name)

@@ -227,6 +227,33 @@ def check_fp8_brute(seed=12):
     check_brute(spec, seed)
 
 
+def check_int8_table():
+    # every byte against torch's int8 view of it (two's complement)
+    codes = np.arange(256, dtype=np.uint8)
+    lib = torch.from_numpy(codes).view(torch.int8).to(torch.float64).numpy()
+    assert np.array_equal(R.int8_codes_to_f64(codes), lib)
+    assert R.int8_codes_to_f64(np.array([0x7F, 0x80, 0xFF], np.uint8)).tolist() == [127.0, -128.0, -1.0]
+
+
+def check_int8_brute(seed=14):
+    spec = tiny_spec(layout="paged", lengths=(16, 11), page_size=4, kv_dtype="int8", topk=16,
+                     topk_mode="random_masked", gate=True, s_q=2, causal=True)
+    check_brute(spec, seed)
+
+
+def check_int8_quantiser_round_trip():
+    # the generator's int8 codes times their scale recover every input within
+    # half a step, and the absmax element lands exactly on +-127
+    rng = np.random.default_rng(15)
+    x = rng.standard_normal((64, 3, 16)).astype(np.float32)
+    amax = np.abs(x).max(axis=(0, 2))
+    s = (amax / np.float32(127.0)).astype(np.float32)
+    codes = gi.quantize_int8(x, s[None, :, None])
+    back = R.int8_codes_to_f64(codes) * s[None, :, None]
+    assert np.all(np.abs(back - x) <= s[None, :, None] * 0.5 + 1e-6)
+    assert set(np.abs(R.int8_codes_to_f64(codes)).max(axis=(0, 2)).tolist()) == {127.0}
+
+
 def check_resolve_rows(seed=13):
     """resolve_rows agrees with the physical rows found by the brute force's
     inverse map, for every layout and with causal masking and top-K."""
@@ -281,6 +308,10 @@ ALL_CHECKS = [
     ("topk_identity_permutation", check_topk_identity_and_permutation),
     ("causal_prefix", check_causal_prefix),
     ("fp8_table", check_fp8_table),
+    ("int8_table", check_int8_table),
+    ("brute_int8", check_int8_brute),
+    ("int8_quantiser_round_trip", check_int8_quantiser_round_trip),
+    ("gqa_equals_mha_paged_int8", lambda: check_gqa_equals_mha(tiny_spec(layout="paged", h_q=8, h_kv=2, kv_dtype="int8", lengths=(9, 5)))),
     ("resolve_rows", check_resolve_rows),
 ]
 

@@ -59,15 +59,16 @@ def test_named_workload_full_size(name, which):
     idx_i = np.array([r[1] for r in rows])
     idx_h = np.array([r[2] for r in rows])
     stats = compare(O[idx_b, idx_i, idx_h], LSE[idx_b, idx_h, idx_i], Oref[idx_b, idx_i, idx_h],
-                    Lref[idx_b, idx_h, idx_i], fp8=w.spec.kv_dtype == gi.KV_FP8, label=f"{name} (sampled)")
+                    Lref[idx_b, idx_h, idx_i], fp8=w.spec.kv_dtype in (gi.KV_FP8, gi.KV_INT8), label=f"{name} (sampled)")
     # Properties of every row at any size: finite, and each output is a
     # convex combination of V rows (times a sigmoid <= 1), so |O| never
     # exceeds the largest |V| of its KV head and column (plus bf16 rounding).
     assert np.isfinite(O).all() and np.isfinite(LSE).all()
     s = w.spec
     G_ = s.h_q // s.h_kv
-    if s.kv_dtype == gi.KV_FP8:
-        bound = np.full((s.batch, s.h_kv, s.head_dim), 448.0) * w.v_scale[:, :, None]
+    if s.kv_dtype in (gi.KV_FP8, gi.KV_INT8):
+        code_max = 448.0 if s.kv_dtype == gi.KV_FP8 else 128.0
+        bound = np.full((s.batch, s.h_kv, s.head_dim), code_max) * w.v_scale[:, :, None]
     else:
         vmax = up.v.reshape(-1, s.h_kv, s.head_dim).float().abs().amax(dim=0).cpu().numpy()
         bound = np.broadcast_to(vmax[None], (s.batch, s.h_kv, s.head_dim))

@@ -77,6 +77,10 @@ def _bf16_wrong_shift(bits):
     return b.view(np.float32).astype(np.float64)
 
 
+def _int8_unsigned(codes):
+    return np.asarray(codes, dtype=np.uint8).astype(np.float64)   # sign ignored
+
+
 MUTATIONS = {
     "kv_head_(h//Hkv)%Hkv": ("kv_head", lambda h, hq, hkv: (h // hkv) % hkv),
     "kv_head_h//Hkv": ("kv_head", lambda h, hq, hkv: min(h // hkv, hkv - 1)),
@@ -89,6 +93,7 @@ MUTATIONS = {
     "sigmoid_sign_flipped": ("sigmoid", lambda x: 1.0 / (1.0 + np.exp(x))),
     "fp8_exponent_bias_8": ("e4m3fn_value", _fp8_bias8),
     "bf16_decode_shift_15": ("bf16_bits_to_f64", _bf16_wrong_shift),
+    "int8_read_unsigned": ("int8_codes_to_f64", _int8_unsigned),
 }
 
 
