@@ -160,7 +160,7 @@ def main():
     ap.add_argument("--workload", default=None,
                     choices=["tiny", "long128k", "ragged", "ragged_sq8", "paged", "sparse_fp8",
                              "long_32x8", "long_8x1", "long_64x8_d64", "long_32x2_d256",
-                             "ragged_sq16", "long_sq64", "append_decode", "append_prefill"])
+                             "ragged_sq16", "long_sq64", "sparse_int8", "append_decode", "append_prefill"])
     ap.add_argument("--scale-policy", default=None, choices=["given", "first_block"],
                     help="append: scale policy (default: the workload's)")
     ap.add_argument("--kv-chunk", type=int, default=0, help="force list positions per workgroup")

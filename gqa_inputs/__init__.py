@@ -308,6 +308,9 @@ RAGGED_B32_SQ16 = Spec(name="ragged_b32_32x8_d128_sq16_8k", batch=32, h_q=32, h_
 LONG_SQ64 = Spec(name="long_64x8_d128_sq64_128k", batch=1, h_q=64, h_kv=8, head_dim=128,
                  s_q=64, seqlen=131072, causal=True)
 
+# The sparse FP8 workload's shape with an int8 cache (absmax/127 scales).
+SPARSE_INT8 = dataclasses.replace(SPARSE_FP8, name="sparse_paged_int8_gated_b256_32x8_top512", kv_dtype=KV_INT8)
+
 NAMED = {
     "tiny": (TINY, 1),
     "long128k": (LONG_128K, 2),
@@ -321,6 +324,7 @@ NAMED = {
     "long_32x2_d256": (LONG_32X2_D256, 9),
     "ragged_sq16": (RAGGED_B32_SQ16, 34),
     "long_sq64": (LONG_SQ64, 35),
+    "sparse_int8": (SPARSE_INT8, 36),
 }
 
 

@@ -29,10 +29,10 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgqa_decode.so")
 
 LAYOUT_CONTIGUOUS, LAYOUT_RAGGED, LAYOUT_PAGED = 0, 1, 2
-KV_BF16, KV_FP8_E4M3FN = 0, 1
+KV_BF16, KV_FP8_E4M3FN, KV_INT8 = 0, 1, 2
 GATE_NONE, GATE_ELEMENTWISE, GATE_HEADWISE = 0, 1, 2
 LAYOUTS = {"contiguous": LAYOUT_CONTIGUOUS, "ragged": LAYOUT_RAGGED, "paged": LAYOUT_PAGED}
-KV_DTYPES = {"bf16": KV_BF16, "fp8_e4m3fn": KV_FP8_E4M3FN}
+KV_DTYPES = {"bf16": KV_BF16, "fp8_e4m3fn": KV_FP8_E4M3FN, "int8": KV_INT8}
 GATE_MODES = {"none": GATE_NONE, "elementwise": GATE_ELEMENTWISE, "headwise": GATE_HEADWISE}
 MATH = {"auto": 0, "mfma": 1, "valu": 2}
 SCALE_POLICIES = {"given": 0, "first_block": 1}

@@ -19,7 +19,7 @@
 #include "gqa_device.h"
 
 namespace gqa {
-hipError_t launch_partial(const DecodeArgs& a, int D, bool fp8, int mode, int mb, int rv, int share, dim3 grid,
+hipError_t launch_partial(const DecodeArgs& a, int D, int kvt, int mode, int mb, int rv, int share, dim3 grid,
                           hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_combine(const DecodeArgs& a, int D, dim3 grid, hipStream_t st);
 hipError_t launch_resolve(const DecodeArgs& a, int64_t* out, int list_cap, hipStream_t st);
@@ -90,11 +90,11 @@ gqa_status check_shape(const gqa_decode_params* p) {
   const int64_t rows = (int64_t)(p->h_q / p->h_kv) * p->s_q;
   if (rows > kMaxRows)
     return fail(GQA_ERR_UNSUPPORTED, "(h_q/h_kv)*s_q = %lld query rows per KV head exceeds %d", (long long)rows, kMaxRows);
-  if (rows > 64 && p->kv_dtype == GQA_KV_FP8_E4M3FN && p->head_dim == 64 && p->h_kv % 2 != 0)
-    return fail(GQA_ERR_UNSUPPORTED, "more than 64 rows per KV head with FP8 d = 64 needs an even h_kv");
+  if (rows > 64 && p->kv_dtype != GQA_KV_BF16 && p->head_dim == 64 && p->h_kv % 2 != 0)
+    return fail(GQA_ERR_UNSUPPORTED, "more than 64 rows per KV head with one-byte codes at d = 64 needs an even h_kv");
   if (p->layout < GQA_LAYOUT_CONTIGUOUS || p->layout > GQA_LAYOUT_PAGED)
     return fail(GQA_ERR_INVALID_ARG, "unknown layout %d", p->layout);
-  if (p->kv_dtype != GQA_KV_BF16 && p->kv_dtype != GQA_KV_FP8_E4M3FN)
+  if (p->kv_dtype != GQA_KV_BF16 && p->kv_dtype != GQA_KV_FP8_E4M3FN && p->kv_dtype != GQA_KV_INT8)
     return fail(GQA_ERR_INVALID_ARG, "unknown kv_dtype %d", p->kv_dtype);
   if (p->gate_mode < GQA_GATE_NONE || p->gate_mode > GQA_GATE_HEADWISE)
     return fail(GQA_ERR_INVALID_ARG, "unknown gate_mode %d", p->gate_mode);
@@ -142,6 +142,11 @@ gqa_status check_shape(const gqa_decode_params* p) {
 // rows (each chunk cut at request boundaries inside the kernel) instead of
 // per-request chunks: every workgroup then streams the same number of rows
 // whatever the mix of lengths.
+// K/V stored as one-byte codes (FP8 or int8) with per-(request, head) scales.
+bool one_byte(const gqa_decode_params* p) { return p->kv_dtype != GQA_KV_BF16; }
+static_assert(GQA_KV_BF16 == gqa::kKvBf16 && GQA_KV_FP8_E4M3FN == gqa::kKvFp8 && GQA_KV_INT8 == gqa::kKvInt8,
+              "the public K/V type enum is the kernels' template argument");
+
 bool packed_mode(const gqa_decode_params* p) { return p->layout == GQA_LAYOUT_RAGGED && p->topk == 0; }
 
 // Bytes of the fp32 partial outputs (the LSE partials follow, rounded up to
@@ -190,7 +195,7 @@ Tiling plan_tiling(const gqa_decode_params* p, int rows, int math) {
     }
     return t;
   }
-  const int loads = p->head_dim * (p->kv_dtype == GQA_KV_FP8_E4M3FN ? 1 : 2) / 32;  // per tile and tensor
+  const int loads = p->head_dim * (one_byte(p) ? 1 : 2) / 32;  // per tile and tensor
   if (loads % 4 == 0) {
     t.share = 4;
     t.hpw = 1;
@@ -231,7 +236,7 @@ gqa_status make_plan(const gqa_decode_params* p, gqa_decode_plan* plan) {
   // faster with one long round (d = 64: 50.2 against 53.0 us; FP8 d = 128:
   // 51.4 against 53.0 us at 128K tokens).
   const int occ = plan->math == GQA_MATH_MFMA && tl.share > 1
-                      ? gqa::partial_wgs_per_cu(p->head_dim, p->kv_dtype == GQA_KV_FP8_E4M3FN, tl.mb, 0, tl.share)
+                      ? gqa::partial_wgs_per_cu(p->head_dim, one_byte(p), tl.mb, 0, tl.share)
                       : 1;
   const int64_t groups = (int64_t)(p->h_kv / hpw) * tl.row_groups;  // grid.y: head groups x row groups
   if (groups > 65535) return fail(GQA_ERR_UNSUPPORTED, "h_kv %d with %d row groups exceeds the grid", p->h_kv, tl.row_groups);
@@ -255,14 +260,14 @@ gqa_status make_plan(const gqa_decode_params* p, gqa_decode_plan* plan) {
       chunk = std::min<int64_t>(chunk, round_up(std::max<int64_t>(L, 1), 32));
       if (indirect) {
         // the row table (8 bytes per position) must fit beside the tiles
-        const size_t tiles = gqa::partial_lds_bytes(p->head_dim, p->kv_dtype == GQA_KV_FP8_E4M3FN, false, 0);
+        const size_t tiles = gqa::partial_lds_bytes(p->head_dim, one_byte(p), false, 0);
         chunk = std::min<int64_t>(chunk, (int64_t)((kMaxLdsPerWorkgroup - tiles) / 8 / 128 * 128));
       }
     }
   }
   // Shared memory of one partial workgroup (per-wave K/V tiles plus the
   // row table of paged / top-K chunks) must fit a workgroup's LDS.
-  const size_t lds = gqa::partial_lds_bytes(p->head_dim, p->kv_dtype == GQA_KV_FP8_E4M3FN, indirect, (int)chunk);
+  const size_t lds = gqa::partial_lds_bytes(p->head_dim, one_byte(p), indirect, (int)chunk);
   if (lds > kMaxLdsPerWorkgroup)
     return fail(GQA_ERR_UNSUPPORTED, "kv_chunk %lld needs %zu bytes of LDS per workgroup (limit %zu)",
                 (long long)chunk, lds, kMaxLdsPerWorkgroup);
@@ -442,7 +447,7 @@ gqa_status gqa_decode_run(const gqa_decode_params* p, const void* q, const void*
   }
   if (p->layout == GQA_LAYOUT_PAGED && !block_table) return fail(GQA_ERR_INVALID_ARG, "paged layout needs block_table");
   if (p->topk > 0 && !topk_idx) return fail(GQA_ERR_INVALID_ARG, "topk > 0 needs topk_idx");
-  if (p->kv_dtype == GQA_KV_FP8_E4M3FN && (!k_scale || !v_scale))
+  if (one_byte(p) && (!k_scale || !v_scale))
     return fail(GQA_ERR_INVALID_ARG, "FP8 K/V need k_scale and v_scale");
   if (p->gate_mode != GQA_GATE_NONE && !gate) return fail(GQA_ERR_INVALID_ARG, "gate_mode set but gate is NULL");
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16) ||
@@ -485,7 +490,7 @@ gqa_status gqa_decode_run(const gqa_decode_params* p, const void* q, const void*
   const Tiling tl = plan_tiling(p, plan.rows, plan.math);
   const dim3 grid(plan.num_splits, (p->h_kv / tl.hpw) * tl.row_groups, a.packed ? 1 : p->batch);
   const bool valu = plan.math == GQA_MATH_VALU;
-  hipError_t e = gqa::launch_partial(a, p->head_dim, p->kv_dtype == GQA_KV_FP8_E4M3FN, mode, valu ? 1 : tl.mb,
+  hipError_t e = gqa::launch_partial(a, p->head_dim, p->kv_dtype, mode, valu ? 1 : tl.mb,
                                      valu ? plan.row_blocks : 0, tl.share, grid, s,
                                      static_cast<hipEvent_t>(p->partial_event_begin),
                                      static_cast<hipEvent_t>(p->partial_event_end));

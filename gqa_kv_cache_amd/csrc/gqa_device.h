@@ -244,6 +244,35 @@ __device__ __forceinline__ void fp8x4_to_bf16x4(uint32_t w, uint32_t& lo, uint32
   hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
 }
 
+// Four int8 codes (one dword, lowest byte first) -> four bf16 in two dwords.
+// Every int8 value is exactly representable in bf16: bias each byte by 128
+// (x ^ 0x80 = x + 128 as an unsigned byte), convert it with
+// v_cvt_f32_ubyte, subtract 128 (exact), and keep the upper halves of the
+// fp32 results (exact: at most 8 significant bits).
+__device__ __forceinline__ void int8x4_to_bf16x4(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  const uint32_t u = w ^ 0x80808080u;
+  // (float) of a byte extract selects v_cvt_f32_ubyte0..3
+  const float f0 = (float)(u & 0xffu) - 128.f;
+  const float f1 = (float)((u >> 8) & 0xffu) - 128.f;
+  const float f2 = (float)((u >> 16) & 0xffu) - 128.f;
+  const float f3 = (float)(u >> 24) - 128.f;
+  // v_perm_b32: bytes 2,3 of the second operand, then bytes 2,3 of the first
+  lo = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, f1), __builtin_bit_cast(uint32_t, f0), 0x07060302u);
+  hi = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, f3), __builtin_bit_cast(uint32_t, f2), 0x07060302u);
+}
+
+// Stored K/V element types; one-byte codes carry a scale per (request, KV head).
+constexpr int kKvBf16 = 0, kKvFp8 = 1, kKvInt8 = 2;
+
+template <int KVT>
+__device__ __forceinline__ void codes4_to_bf16x4(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  static_assert(KVT == kKvFp8 || KVT == kKvInt8, "one-byte codes");
+  if constexpr (KVT == kKvFp8)
+    fp8x4_to_bf16x4(w, lo, hi);
+  else
+    int8x4_to_bf16x4(w, lo, hi);
+}
+
 // Two bf16 products plus c, accumulated in fp32 (v_dot2_f32_bf16).
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);

@@ -44,9 +44,9 @@
 
 namespace gqa {
 
-template <int D, bool FP8>
+template <int D, bool Q8>
 struct TileShape {
-  static constexpr int ESZ = FP8 ? 1 : 2;
+  static constexpr int ESZ = Q8 ? 1 : 2;
   static constexpr int RB = D * ESZ;          // bytes of one head in one token row
   static constexpr int CPR = RB / 16;         // 16-byte chunks per row (16, 8 or 4)
   static constexpr int TPI = 64 / CPR;        // tokens per wave-wide load (4, 8 or 16)
@@ -72,9 +72,9 @@ __host__ __device__ constexpr size_t table_bytes(bool indirect, int chunk) { ret
 // Contraction slot -> d.  K-step kk, lane group qd covers d = qk_d(kk, qd)
 // .. +7.  bf16: one 16-byte chunk per k-step (chunk 4 kk + qd); FP8: one
 // 16-byte chunk (16 codes, chunk 4 (kk / 2) + qd) feeds two k-steps.
-template <bool FP8>
+template <bool Q8>
 __device__ __forceinline__ int qk_d(int kk, int qd) {
-  return FP8 ? (64 * (kk >> 1) + 16 * qd + 8 * (kk & 1)) : (32 * kk + 8 * qd);
+  return Q8 ? (64 * (kk >> 1) + 16 * qd + 8 * (kk & 1)) : (32 * kk + 8 * qd);
 }
 
 // Physical 16-byte chunk of logical chunk c in the K tile row of token tok:
@@ -107,8 +107,8 @@ __device__ __forceinline__ int vblk(int blk, int tok) {
 //             number of rows, however the lengths vary.
 constexpr int kDense = 0, kIndirect = 1, kPacked = 2;
 
-template <int D, bool FP8, int MB, int RV, int SHARE>
-constexpr int partial_min_blocks() { return partial_wgs_per_cu(D, FP8, MB, RV, SHARE); }
+template <int D, bool Q8, int MB, int RV, int SHARE>
+constexpr int partial_min_blocks() { return partial_wgs_per_cu(D, Q8, MB, RV, SHARE); }
 
 // MB: 16-row MFMA blocks (RV = 0).  RV > 0 selects the VALU variant for up
 // to RV query rows (MB = 1): the same loads, LDS staging and pipeline, with
@@ -128,10 +128,11 @@ constexpr int partial_min_blocks() { return partial_wgs_per_cu(D, FP8, MB, RV, S
 // more than 32 rows; a workgroup covers SHARE * MB * 16 rows (row group
 // blockIdx.y / (H_kv / HPW)), and a group of up to 512 rows takes several
 // row groups, each reading the chunk.
-template <int D, bool FP8, int MODE, int MB, int RV, int SHARE>
-__global__ void __launch_bounds__(kPThreads, (partial_min_blocks<D, FP8, MB, RV, SHARE>()))
+template <int D, int KVT, int MODE, int MB, int RV, int SHARE>
+__global__ void __launch_bounds__(kPThreads, (partial_min_blocks<D, KVT != kKvBf16, MB, RV, SHARE>()))
     gqa_partial_kernel(DecodeArgs a) {
-  using TS = TileShape<D, FP8>;
+  constexpr bool Q8 = KVT != kKvBf16;          // one-byte codes (FP8 or int8) with scales
+  using TS = TileShape<D, Q8>;
   constexpr int RB = TS::RB, CPR = TS::CPR, TPI = TS::TPI, NLD = TS::NLD, KK = TS::KK, NB = TS::NB;
   constexpr bool SHARED = SHARE > 1;
   constexpr int NPART = TS::NPART;
@@ -143,13 +144,13 @@ __global__ void __launch_bounds__(kPThreads, (partial_min_blocks<D, FP8, MB, RV,
   constexpr bool INDIRECT = MODE == kIndirect;
   constexpr bool PACKED = MODE == kPacked;
   constexpr bool VALU = RV > 0;
-  constexpr int ELT = FP8 ? 16 : 8;             // elements of one 16-byte chunk
+  constexpr int ELT = Q8 ? 16 : 8;             // elements of one 16-byte chunk
   constexpr int NR = VALU ? RV : MB;            // running-state rows per lane
   static_assert(!VALU || MB == 1, "the VALU variant computes one block of at most 16 rows");
-  static_assert(kPWaves * 16 * D * 4 <= kPWaves * wave_tile_bytes(D, FP8), "accumulators fit in the tiles");
+  static_assert(kPWaves * 16 * D * 4 <= kPWaves * wave_tile_bytes(D, Q8), "accumulators fit in the tiles");
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  __shared__ __attribute__((aligned(16))) unsigned char tiles[kPWaves * wave_tile_bytes(D, FP8)];
+  __shared__ __attribute__((aligned(16))) unsigned char tiles[kPWaves * wave_tile_bytes(D, Q8)];
   __shared__ float wstat[2 * kPWaves * 16];
 
   const int lane = threadIdx.x & 63;
@@ -258,7 +259,7 @@ __global__ void __launch_bounds__(kPThreads, (partial_min_blocks<D, FP8, MB, RV,
       const uint16_t* qrow = a.q + ((int64_t)(b * a.s_q + i) * a.h_q + h) * D;
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk)
-        qop[mb][kk] = *reinterpret_cast<const u32x4*>(qrow + qk_d<FP8>(kk, qd));
+        qop[mb][kk] = *reinterpret_cast<const u32x4*>(qrow + qk_d<Q8>(kk, qd));
     } else {
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) qop[mb][kk] = u32x4{0u, 0u, 0u, 0u};
@@ -266,7 +267,7 @@ __global__ void __launch_bounds__(kPThreads, (partial_min_blocks<D, FP8, MB, RV,
   }
 
   float sc = a.scale_log2;
-  if constexpr (FP8) sc *= a.k_scale[b * a.h_kv + g];
+  if constexpr (Q8) sc *= a.k_scale[b * a.h_kv + g];
 
   f32x4 acc[VALU ? 1 : MB][NB];
   float accv[VALU ? RV : 1][ELT];
@@ -287,13 +288,13 @@ __global__ void __launch_bounds__(kPThreads, (partial_min_blocks<D, FP8, MB, RV,
 
   // Staged K and V tiles: one per wave, or (rows shared) two per head,
   // alternating by tile parity.
-  unsigned char* wtiles = tiles + (SHARED ? 2 * hs : wave) * wave_tile_bytes(D, FP8);
+  unsigned char* wtiles = tiles + (SHARED ? 2 * hs : wave) * wave_tile_bytes(D, Q8);
   u32x4* kt = reinterpret_cast<u32x4*>(wtiles);
-  uint16_t* vt = reinterpret_cast<uint16_t*>(wtiles + ktile_chunks(D, FP8) * 16);
+  uint16_t* vt = reinterpret_cast<uint16_t*>(wtiles + ktile_chunks(D, Q8) * 16);
   auto use_buffer = [&](int parity) __attribute__((always_inline)) {
-    unsigned char* t = tiles + (2 * hs + parity) * wave_tile_bytes(D, FP8);
+    unsigned char* t = tiles + (2 * hs + parity) * wave_tile_bytes(D, Q8);
     kt = reinterpret_cast<u32x4*>(t);
-    vt = reinterpret_cast<uint16_t*>(t + ktile_chunks(D, FP8) * 16);
+    vt = reinterpret_cast<uint16_t*>(t + ktile_chunks(D, Q8) * 16);
   };
   const size_t head_off = (size_t)g * RB;
   const size_t row_bytes = (size_t)a.h_kv * RB;
@@ -338,13 +339,13 @@ __global__ void __launch_bounds__(kPThreads, (partial_min_blocks<D, FP8, MB, RV,
       const int tok = i * TPI + ltok;
       kt[tok * CPR + kchunk<CPR>(lch, tok)] = kr[ii];
       uint16_t* vrow = vt + tok * D;
-      if constexpr (FP8) {
+      if constexpr (Q8) {
         // 16 codes = d [16 lch, +16) = one 16-element block
         uint32_t x0, x1, x2, x3, y0, y1, y2, y3;
-        fp8x4_to_bf16x4(vr[ii][0], x0, x1);
-        fp8x4_to_bf16x4(vr[ii][1], x2, x3);
-        fp8x4_to_bf16x4(vr[ii][2], y0, y1);
-        fp8x4_to_bf16x4(vr[ii][3], y2, y3);
+        codes4_to_bf16x4<KVT>(vr[ii][0], x0, x1);
+        codes4_to_bf16x4<KVT>(vr[ii][1], x2, x3);
+        codes4_to_bf16x4<KVT>(vr[ii][2], y0, y1);
+        codes4_to_bf16x4<KVT>(vr[ii][3], y2, y3);
         uint16_t* dst = vrow + 16 * vblk<D>(lch, tok);
         *reinterpret_cast<u32x4*>(dst) = u32x4{x0, x1, x2, x3};
         *reinterpret_cast<u32x4*>(dst + 8) = u32x4{y0, y1, y2, y3};
@@ -374,14 +375,14 @@ __global__ void __launch_bounds__(kPThreads, (partial_min_blocks<D, FP8, MB, RV,
       const int tok = hb * 16 + m16;
       u32x4 kop[KK];
 #pragma unroll
-      for (int j = 0; j < (FP8 ? KK / 2 : KK); ++j) {
+      for (int j = 0; j < (Q8 ? KK / 2 : KK); ++j) {
         const u32x4 c = kt[tok * CPR + kchunk<CPR>(4 * j + qd, tok)];
-        if constexpr (FP8) {
+        if constexpr (Q8) {
           uint32_t x0, x1, x2, x3, y0, y1, y2, y3;
-          fp8x4_to_bf16x4(c[0], x0, x1);
-          fp8x4_to_bf16x4(c[1], x2, x3);
-          fp8x4_to_bf16x4(c[2], y0, y1);
-          fp8x4_to_bf16x4(c[3], y2, y3);
+          codes4_to_bf16x4<KVT>(c[0], x0, x1);
+          codes4_to_bf16x4<KVT>(c[1], x2, x3);
+          codes4_to_bf16x4<KVT>(c[2], y0, y1);
+          codes4_to_bf16x4<KVT>(c[3], y2, y3);
           kop[2 * j] = u32x4{x0, x1, x2, x3};
           kop[2 * j + 1] = u32x4{y0, y1, y2, y3};
         } else {
@@ -492,9 +493,9 @@ __global__ void __launch_bounds__(kPThreads, (partial_min_blocks<D, FP8, MB, RV,
       const int tok = i * TPI + ltok;
       const u32x4 c = kt[tok * CPR + kchunk<CPR>(lch, tok)];
       uint32_t kp[ELT / 2];
-      if constexpr (FP8) {
+      if constexpr (Q8) {
 #pragma unroll
-        for (int w = 0; w < 4; ++w) fp8x4_to_bf16x4(c[w], kp[2 * w], kp[2 * w + 1]);
+        for (int w = 0; w < 4; ++w) codes4_to_bf16x4<KVT>(c[w], kp[2 * w], kp[2 * w + 1]);
       } else {
 #pragma unroll
         for (int w = 0; w < 4; ++w) kp[w] = c[w];
@@ -744,7 +745,7 @@ __global__ void __launch_bounds__(kPThreads, (partial_min_blocks<D, FP8, MB, RV,
       if (r >= a.rows) continue;
       const float m = mrun[mb], l = lrun[mb];
       const bool empty = (m == -INFINITY);
-      const float inv = empty ? 0.f : (FP8 ? a.v_scale[b * a.h_kv + g] : 1.f) / l;
+      const float inv = empty ? 0.f : (Q8 ? a.v_scale[b * a.h_kv + g] : 1.f) / l;
       const float lse2 = empty ? -INFINITY : m + __log2f(l);
       const int i = r / a.group;
       const int h = g * a.group + (r - i * a.group);
@@ -848,7 +849,7 @@ __global__ void __launch_bounds__(kPThreads, (partial_min_blocks<D, FP8, MB, RV,
               o[4 + c] += e * x1[c];
             }
           }
-          const float inv = (FP8 ? a.v_scale[b * a.h_kv + gg] : 1.f) / sum;
+          const float inv = (Q8 ? a.v_scale[b * a.h_kv + gg] : 1.f) / sum;
 #pragma unroll
           for (int e = 0; e < 8; ++e) o[e] *= inv;
           lse2 = M + __log2f(sum);
@@ -1050,59 +1051,59 @@ __global__ void __launch_bounds__(kThreads) gqa_resolve_kernel(DecodeArgs a, int
 
 // ev0 / ev1 (may be null): events stamped by the dispatch itself at the
 // kernel's start and end, so they time the kernel alone.
-template <int D, bool FP8, int MODE, int MB, int RV, int SHARE = 1>
+template <int D, int KVT, int MODE, int MB, int RV, int SHARE = 1>
 static hipError_t launch_partial_t(const DecodeArgs& a, dim3 grid, hipStream_t st, hipEvent_t ev0,
                                    hipEvent_t ev1) {
   const size_t lds = table_bytes(MODE == kIndirect, a.chunk);
-  hipExtLaunchKernelGGL((gqa_partial_kernel<D, FP8, MODE, MB, RV, SHARE>), grid, dim3(kPThreads), lds, st, ev0, ev1, 0,
+  hipExtLaunchKernelGGL((gqa_partial_kernel<D, KVT, MODE, MB, RV, SHARE>), grid, dim3(kPThreads), lds, st, ev0, ev1, 0,
                         a);
   return hipGetLastError();
 }
 
 // rv > 0: the VALU variant for up to rv rows (1, 2, 4 or 8); share = 2:
 // two waves per head, one 16-row block each (d = 256); else mb MFMA blocks.
-template <int D, bool FP8, int MODE>
+template <int D, int KVT, int MODE>
 static hipError_t launch_mb(const DecodeArgs& a, int mb, int rv, int share, dim3 grid, hipStream_t st,
                             hipEvent_t ev0, hipEvent_t ev1) {
   // Row sharing: the combinations the planner picks (share_tiling in the
   // host code) and no others.
-  constexpr int NLD = TileShape<D, FP8>::NLD;
+  constexpr int NLD = TileShape<D, KVT != kKvBf16>::NLD;
   if (share == 2) {
-    if constexpr (D == 256) return launch_partial_t<D, FP8, MODE, 1, 0, 2>(a, grid, st, ev0, ev1);
-    if constexpr (NLD == 2) return launch_partial_t<D, FP8, MODE, 2, 0, 2>(a, grid, st, ev0, ev1);
+    if constexpr (D == 256) return launch_partial_t<D, KVT, MODE, 1, 0, 2>(a, grid, st, ev0, ev1);
+    if constexpr (NLD == 2) return launch_partial_t<D, KVT, MODE, 2, 0, 2>(a, grid, st, ev0, ev1);
     return hipErrorInvalidValue;
   }
   if (share == 4) {
     if constexpr (NLD % 4 == 0) {
-      if (mb == 1) return launch_partial_t<D, FP8, MODE, 1, 0, 4>(a, grid, st, ev0, ev1);
-      if constexpr (D <= 128) return launch_partial_t<D, FP8, MODE, 2, 0, 4>(a, grid, st, ev0, ev1);
+      if (mb == 1) return launch_partial_t<D, KVT, MODE, 1, 0, 4>(a, grid, st, ev0, ev1);
+      if constexpr (D <= 128) return launch_partial_t<D, KVT, MODE, 2, 0, 4>(a, grid, st, ev0, ev1);
     }
     return hipErrorInvalidValue;
   }
   if constexpr (D <= 128) {
     if (rv > 0) {
       switch (rv) {
-        case 1: return launch_partial_t<D, FP8, MODE, 1, 1>(a, grid, st, ev0, ev1);
-        case 2: return launch_partial_t<D, FP8, MODE, 1, 2>(a, grid, st, ev0, ev1);
-        case 4: return launch_partial_t<D, FP8, MODE, 1, 4>(a, grid, st, ev0, ev1);
-        default: return launch_partial_t<D, FP8, MODE, 1, 8>(a, grid, st, ev0, ev1);
+        case 1: return launch_partial_t<D, KVT, MODE, 1, 1>(a, grid, st, ev0, ev1);
+        case 2: return launch_partial_t<D, KVT, MODE, 1, 2>(a, grid, st, ev0, ev1);
+        case 4: return launch_partial_t<D, KVT, MODE, 1, 4>(a, grid, st, ev0, ev1);
+        default: return launch_partial_t<D, KVT, MODE, 1, 8>(a, grid, st, ev0, ev1);
       }
     }
   }
   switch (mb) {
-    case 1: return launch_partial_t<D, FP8, MODE, 1, 0>(a, grid, st, ev0, ev1);
-    case 2: return launch_partial_t<D, FP8, MODE, 2, 0>(a, grid, st, ev0, ev1);
-    default: return launch_partial_t<D, FP8, MODE, 4, 0>(a, grid, st, ev0, ev1);
+    case 1: return launch_partial_t<D, KVT, MODE, 1, 0>(a, grid, st, ev0, ev1);
+    case 2: return launch_partial_t<D, KVT, MODE, 2, 0>(a, grid, st, ev0, ev1);
+    default: return launch_partial_t<D, KVT, MODE, 4, 0>(a, grid, st, ev0, ev1);
   }
 }
 
-template <int D, bool FP8>
+template <int D, int KVT>
 static hipError_t launch_mode(const DecodeArgs& a, int mode, int mb, int rv, int share, dim3 grid,
                               hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   switch (mode) {
-    case kIndirect: return launch_mb<D, FP8, kIndirect>(a, mb, rv, share, grid, st, ev0, ev1);
-    case kPacked: return launch_mb<D, FP8, kPacked>(a, mb, rv, share, grid, st, ev0, ev1);
-    default: return launch_mb<D, FP8, kDense>(a, mb, rv, share, grid, st, ev0, ev1);
+    case kIndirect: return launch_mb<D, KVT, kIndirect>(a, mb, rv, share, grid, st, ev0, ev1);
+    case kPacked: return launch_mb<D, KVT, kPacked>(a, mb, rv, share, grid, st, ev0, ev1);
+    default: return launch_mb<D, KVT, kDense>(a, mb, rv, share, grid, st, ev0, ev1);
   }
 }
 
@@ -1110,17 +1111,23 @@ size_t partial_lds_bytes(int D, bool fp8, bool indirect, int chunk) {
   return (size_t)kPWaves * wave_tile_bytes(D, fp8) + 2 * kPWaves * 16 * 4 + table_bytes(indirect, chunk);
 }
 
-// mode: 0 dense, 1 indirect (paged / top-K), 2 packed ragged.
-hipError_t launch_partial(const DecodeArgs& a, int D, bool fp8, int mode, int mb, int rv, int share, dim3 grid,
+template <int D>
+static hipError_t launch_kvt(const DecodeArgs& a, int kvt, int mode, int mb, int rv, int share, dim3 grid,
+                             hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+  switch (kvt) {
+    case kKvFp8: return launch_mode<D, kKvFp8>(a, mode, mb, rv, share, grid, st, ev0, ev1);
+    case kKvInt8: return launch_mode<D, kKvInt8>(a, mode, mb, rv, share, grid, st, ev0, ev1);
+    default: return launch_mode<D, kKvBf16>(a, mode, mb, rv, share, grid, st, ev0, ev1);
+  }
+}
+
+// mode: 0 dense, 1 indirect (paged / top-K), 2 packed ragged.  kvt: the
+// stored K/V type (kKvBf16, kKvFp8, kKvInt8).
+hipError_t launch_partial(const DecodeArgs& a, int D, int kvt, int mode, int mb, int rv, int share, dim3 grid,
                           hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
-  if (D == 256)
-    return fp8 ? launch_mode<256, true>(a, mode, mb, rv, share, grid, st, ev0, ev1)
-               : launch_mode<256, false>(a, mode, mb, rv, share, grid, st, ev0, ev1);
-  if (D == 128)
-    return fp8 ? launch_mode<128, true>(a, mode, mb, rv, share, grid, st, ev0, ev1)
-               : launch_mode<128, false>(a, mode, mb, rv, share, grid, st, ev0, ev1);
-  return fp8 ? launch_mode<64, true>(a, mode, mb, rv, share, grid, st, ev0, ev1)
-             : launch_mode<64, false>(a, mode, mb, rv, share, grid, st, ev0, ev1);
+  if (D == 256) return launch_kvt<256>(a, kvt, mode, mb, rv, share, grid, st, ev0, ev1);
+  if (D == 128) return launch_kvt<128>(a, kvt, mode, mb, rv, share, grid, st, ev0, ev1);
+  return launch_kvt<64>(a, kvt, mode, mb, rv, share, grid, st, ev0, ev1);
 }
 
 hipError_t launch_combine(const DecodeArgs& a, int D, dim3 grid, hipStream_t st) {

@@ -17,7 +17,7 @@
  *
  * The cache can be contiguous, ragged (packed with offsets) or paged
  * through a block table; a per-request top-K list can restrict attention to
- * selected tokens; K/V can be FP8 E4M3FN with one fp32 scale per
+ * selected tokens; K/V can be FP8 E4M3FN (or int8) with one fp32 scale per
  * (request, KV head); and the output can be multiplied by sigmoid(gate).
  * These follow "Sparse paged GQA decode attention with FP8 KV cache on
  * SM89" (sections "Workload" and "Implementations").
@@ -68,7 +68,14 @@ enum {
                                 block_table[b, t / page_size] * page_size + t % page_size           */
 };
 
-enum { GQA_KV_BF16 = 0, GQA_KV_FP8_E4M3FN = 1 };
+/* Stored K/V element types.  FP8 E4M3FN and int8 (two's complement) are
+ * codes with one fp32 scale per (request, KV head): the stored value is
+ * code * k_scale[b, g] (K) or code * v_scale[b, g] (V).  The kernels convert
+ * codes to bf16 tile by tile in registers, never the whole cache (the int8
+ * KV-cache section of "Profiling down to the register, then an extension
+ * that broke my assumptions twice" reports what a whole-cache conversion
+ * costs).                                                                    */
+enum { GQA_KV_BF16 = 0, GQA_KV_FP8_E4M3FN = 1, GQA_KV_INT8 = 2 };
 
 /* GQA_GATE_ELEMENTWISE: gate bf16 [B, S_q, H_q, d], O *= sigmoid(gate).
  * GQA_GATE_HEADWISE:    gate bf16 [B, S_q, H_q],    one value per head.     */
@@ -144,7 +151,7 @@ gqa_status gqa_decode_workspace_size(const gqa_decode_params* p, size_t* bytes);
 
 /* Decode attention.
  *   q           bf16 [B, S_q, H_q, d]
- *   k_cache,    bf16 or FP8 E4M3FN codes, layout p->layout (see above),
+ *   k_cache,    bf16, or FP8 E4M3FN or int8 codes, layout p->layout (see above),
  *   v_cache     same layout, dtype and size as k_cache
  *   seqlens     int32 [B]   n_b (contiguous, paged); NULL for ragged
  *   cu_seqlens  int32 [B+1] ragged offsets (n_b = cu[b+1] - cu[b]); else NULL
@@ -152,7 +159,7 @@ gqa_status gqa_decode_workspace_size(const gqa_decode_params* p, size_t* bytes);
  *   topk_idx    int32 [B, topk] logical token positions (topk > 0); else NULL.
  *               Entries outside [0, n_b) are masked; duplicates count once
  *               per occurrence.
- *   k_scale,    fp32 [B, H_kv] (FP8 only, else NULL): stored codes mean
+ *   k_scale,    fp32 [B, H_kv] (FP8 and int8, else NULL): stored codes mean
  *   v_scale     code_value * scale
  *   gate        bf16, shape by p->gate_mode; NULL when GQA_GATE_NONE
  *   o           bf16 [B, S_q, H_q, d], written in full

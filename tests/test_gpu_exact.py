@@ -67,7 +67,7 @@ def test_resolve_rows_bit_exact(idx):
     assert torch.equal(got, torch.from_numpy(want)), f"case {idx}: {(got.numpy() != want).sum()} slots differ"
 
 
-def _probe(w, rng, fp8=False):
+def _probe(w, rng, fp8=False, int8=False):
     """Rewrite q, K, V of a workload into a one-hot probe.  Returns the
     expected O (bf16 bits or FP8 codes of the target V rows)."""
     s = w.spec
@@ -79,6 +79,9 @@ def _probe(w, rng, fp8=False):
     if fp8:
         one, big = 0x4100, 0x7E                # q = bf16 8.0, K = E4M3FN 448.0
         kf[:, :, 0] = 0
+    elif int8:
+        one, big = 0x4200, 0x7F                # q = bf16 32.0, K = int8 127
+        kf[:, :, 0] = 0
     else:
         one, big = 0x3F80, 0x4500              # bf16 1.0 and 2048.0
         kf[:, :, 0] = 0
@@ -87,7 +90,7 @@ def _probe(w, rng, fp8=False):
     # V[row, g, :] encodes (row, g) in base-16 (FP8) or base-256 (bf16) digits
     nrow = vf.shape[0]
     rid = np.arange(nrow, dtype=np.int64)
-    base = 16 if fp8 else 256
+    base = 16 if (fp8 or int8) else 256
     digits = np.zeros((nrow, Hkv, d), dtype=np.int64)
     for c in range(d):
         if c < 4:
@@ -99,6 +102,8 @@ def _probe(w, rng, fp8=False):
     if fp8:
         codes = torch.from_numpy(digits.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
         vf[...] = codes
+    elif int8:
+        vf[...] = digits.astype(np.uint8)      # 0..15: the int8 code is the value
     else:
         vf[...] = gi.f32_to_bf16_bits(digits.astype(np.float32))
     expect = {}
@@ -111,7 +116,7 @@ def _probe(w, rng, fp8=False):
             target = int(rows[b, 0, slot])
             kf[target, g, 0] = big
             expect[(b, g)] = target
-    if fp8:
+    if fp8 or int8:
         w.k_scale[...] = 1.0
         w.v_scale[...] = 1.0
     return expect

@@ -35,7 +35,7 @@ def _sample_rows(w, k, seed):
 # per KV head also with the other math path.
 FULL_CASES = [(n, "auto") for n in ("tiny", "long128k", "ragged", "ragged_sq8", "paged", "sparse_fp8",
                                      "long_32x8", "long_8x1", "long_64x8_d64", "long_32x2_d256",
-                                     "ragged_sq16", "long_sq64")] + \
+                                     "ragged_sq16", "long_sq64", "sparse_int8")] + \
              [(n, "other") for n in ("tiny", "ragged", "paged", "sparse_fp8")]
 
 
