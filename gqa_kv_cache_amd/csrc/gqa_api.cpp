@@ -178,7 +178,7 @@ static_assert(gqa::kPWaves == 4, "row sharing is laid out for 4 waves per workgr
 // tiles.  17-32 rows: two blocks per wave, except d = 256 (two blocks of
 // d = 256 do not fit a wave's registers), where a head's two waves split
 // the rows and share the tiles through LDS (even H_kv).  More than 32 rows:
-// a head's four waves split the rows, one block each up to 64 rows, two
+// a head's four waves split the rows, one block each up to 256 rows, two
 // (d <= 128) beyond, and groups of more rows than one workgroup covers
 // take several row groups.  FP8 d = 64 tiles are two loads per tensor, so
 // there two waves per head split the rows, two blocks each.
@@ -199,7 +199,12 @@ Tiling plan_tiling(const gqa_decode_params* p, int rows, int math) {
   if (loads % 4 == 0) {
     t.share = 4;
     t.hpw = 1;
-    t.mb = (rows > 64 && p->head_dim <= 128) ? 2 : 1;
+    // One block per wave up to 256 rows (more row groups, two workgroups
+    // per CU), two beyond (d <= 128), where the row groups' repeated reads
+    // of the chunk cost more than the extra residency gains.  MI355X, one
+    // process: 128 rows 93.6 -> 81.5 us and 256 rows 325 -> 287 us with one
+    // block; 512 rows 643 us with two against 783 us with one.
+    t.mb = (rows > 256 && p->head_dim <= 128) ? 2 : 1;
     t.row_groups = (int)cdiv(rows, 64 * t.mb);
   } else if (p->h_kv % 2 == 0) {
     t.share = 2;

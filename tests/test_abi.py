@@ -239,15 +239,16 @@ def test_append_batch_zero_is_a_no_op():
 
 
 def test_plan_tiling_of_large_groups():
-    # rows -> 16-row blocks per KV head: up to 64 rows one block per wave of
-    # four; beyond, two blocks per wave (d <= 128) in row groups of 128
+    # rows -> 16-row blocks per KV head: one block per wave of four in row
+    # groups of 64 up to 256 rows; beyond, two blocks per wave (d <= 128) in
+    # row groups of 128
     def plan(**kw):
         d = dict(batch=1, s_q=1, h_q=8, h_kv=8, head_dim=128, max_seqlen_kv=4096, seq_capacity=4096,
                  kv_rows=4096, num_cus=256)
         d.update(kw)
         return G.gqa_decode_make_plan(G.make_params(**d))
     assert plan(h_q=48, h_kv=1)["row_blocks"] == 4                       # 48 rows: 4 waves x 1 block
-    assert plan(h_q=64, h_kv=8, s_q=16)["row_blocks"] == 8               # 128 rows: 4 x 2
+    assert plan(h_q=64, h_kv=8, s_q=16)["row_blocks"] == 8               # 128 rows: 4 x 1, two row groups
     assert plan(h_q=64, h_kv=8, s_q=64)["row_blocks"] == 32              # 512 rows: 4 row groups of 128
     assert plan(h_q=64, h_kv=8, s_q=64, head_dim=256)["row_blocks"] == 32  # d256: 8 groups of 64
     assert plan(h_q=32, h_kv=2, s_q=2, head_dim=256)["row_blocks"] == 2  # two waves x 1 block

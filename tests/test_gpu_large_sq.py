@@ -32,10 +32,10 @@ SHAPES = [
     (4, 2, 16, 128),    # 32 rows: two blocks in one wave
     (6, 2, 16, 128),    # 48 rows: four waves, one block each
     (8, 2, 16, 128),    # 64 rows
-    (10, 2, 13, 128),   # 65 rows: four waves, two blocks each
-    (16, 2, 16, 128),   # 128 rows
-    (18, 2, 16, 128),   # 144 rows: two row groups
-    (64, 8, 64, 128),   # 512 rows: four row groups
+    (10, 2, 13, 128),   # 65 rows: four waves, one block each, two row groups
+    (16, 2, 16, 128),   # 128 rows: two row groups
+    (18, 2, 16, 128),   # 144 rows: three row groups
+    (64, 8, 64, 128),   # 512 rows: two blocks per wave, four row groups
     (8, 1, 64, 64),     # 512 rows, d 64
     (8, 8, 16, 64),     # 16 rows, d 64
     (12, 4, 16, 64),    # 48 rows, d 64
