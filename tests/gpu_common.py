@@ -125,7 +125,8 @@ def compare(O, LSE, Oref, Lref, *, fp8=False, mask=None, label=""):
     rel = float(np.linalg.norm(d_o) / nref) if nref > 0 else float(np.linalg.norm(d_o))
     a = O[orow].ravel()
     b = Oref[orow].ravel()
-    cos = float(a @ b / (np.linalg.norm(a) * np.linalg.norm(b))) if np.linalg.norm(b) > 0 else 1.0
+    na, nb = float(np.linalg.norm(a)), float(np.linalg.norm(b))
+    cos = float(a @ b / (na * nb)) if na > 0 and nb > 0 else (1.0 if na == nb else 0.0)
     stats = dict(o_max_abs=o_err, lse_max_abs=lse_err, o_rel_l2=rel, o_cosine=cos)
     log(f"  [{label}] {stats}")
     atol = O_ATOL_FP8 if fp8 else O_ATOL_BF16
