@@ -249,11 +249,12 @@ def decode(q, k_cache, v_cache, *, h_kv: Optional[int] = None, seqlens=None, cu_
            gate_mode: Optional[str] = None, causal: bool = False,
            softmax_scale: Optional[float] = None, max_seqlen_kv: Optional[int] = None,
            layout: Optional[str] = None, kv_chunk: int = 0, out=None, lse=None, workspace=None,
-           stream=None):
+           stream=None, kv_dtype: Optional[str] = None):
     """Allocate O / LSE / workspace with torch and run one decode call.
 
-    q: bf16 [B, S_q, H_q, d].  k_cache / v_cache: bf16, or uint8 /
-    float8_e4m3fn codes, as [B, S_cap, H_kv, d] (contiguous),
+    q: bf16 [B, S_q, H_q, d].  k_cache / v_cache: bf16, float8_e4m3fn or
+    int8 tensors (or uint8 bytes, read as FP8 codes unless kv_dtype says
+    "int8"), as [B, S_cap, H_kv, d] (contiguous),
     [N, H_kv, d] (ragged, with cu_seqlens) or [pages, P, H_kv, d] (paged,
     with block_table).  Returns (O bf16 [B, S_q, H_q, d], LSE fp32
     [B, H_q, S_q]).  ``max_seqlen_kv`` is required for the ragged layout;
@@ -265,7 +266,13 @@ def decode(q, k_cache, v_cache, *, h_kv: Optional[int] = None, seqlens=None, cu_
         layout = "paged" if block_table is not None else ("ragged" if cu_seqlens is not None else "contiguous")
     if h_kv is None:
         h_kv = k_cache.shape[-2]
-    fp8 = k_cache.dtype in (torch.uint8, getattr(torch, "float8_e4m3fn", None))
+    if kv_dtype is None:
+        if k_cache.dtype == torch.int8:
+            kv_dtype = "int8"
+        elif k_cache.dtype in (torch.uint8, getattr(torch, "float8_e4m3fn", None)):
+            kv_dtype = "fp8_e4m3fn"
+        else:
+            kv_dtype = "bf16"
     if layout == "contiguous":
         cap = k_cache.shape[1]
         kv_rows = k_cache.shape[0] * cap
@@ -283,7 +290,7 @@ def decode(q, k_cache, v_cache, *, h_kv: Optional[int] = None, seqlens=None, cu_
     if gate_mode is None:
         gate_mode = "none" if gate is None else ("headwise" if gate.dim() == 3 else "elementwise")
     params = make_params(batch=B, s_q=Sq, h_q=Hq, h_kv=h_kv, head_dim=d, layout=layout,
-                         kv_dtype="fp8_e4m3fn" if fp8 else "bf16", causal=causal, max_seqlen_kv=mx,
+                         kv_dtype=kv_dtype, causal=causal, max_seqlen_kv=mx,
                          seq_capacity=cap, kv_rows=max(kv_rows, 1), page_size=page,
                          max_pages_per_seq=mpp,
                          topk=0 if topk_idx is None else topk_idx.shape[1], gate_mode=gate_mode,
