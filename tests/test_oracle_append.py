@@ -174,6 +174,25 @@ def test_append_writes_only_target_rows_paged():
             assert np.all(k2[pg, sl] == want), (pg, sl)
 
 
+def test_positions_without_a_row_are_not_written():
+    B, Hkv, d, cap = 2, 1, 8, 4
+    cache = np.full((B, cap, Hkv, d), 0x5555, np.uint16)
+    new = np.full((B, 3, Hkv, d), 0x3F80, np.uint16)          # 1.0
+    k2, _, _, _, lens = A.reference_append(k_cache=cache, v_cache=cache, k_new=new, v_new=new, seqlens=[2, 4],
+                                           layout=R.CONTIGUOUS, kv_dtype=R.BF16, capacity=cap)
+    assert np.all(k2[0, 2:] == 0x3F80) and np.all(k2[0, :2] == 0x5555)   # request 0: slots 2, 3; slot 4 is past
+    assert np.all(k2[1] == 0x5555)                                       # request 1 is full: nothing written
+    assert list(lens) == [5, 7]
+    P = 2
+    pool = np.full((3, P, Hkv, d), 0x5555, np.uint16)
+    bt = np.array([[2, 9], [1, 0]], np.int32)                             # page 9 is outside the pool
+    k3, _, _, _, _ = A.reference_append(k_cache=pool, v_cache=pool, k_new=new, v_new=new, seqlens=[1, 3],
+                                        layout=R.PAGED, kv_dtype=R.BF16, block_table=bt, page_size=P)
+    assert np.all(k3[2, 1] == 0x3F80)                                    # request 0, token 1
+    assert np.all(k3[0, 1] == 0x3F80)                                    # request 1, token 3 (page 0, slot 1)
+    assert np.all(k3[1] == 0x5555) and np.all(k3[2, 0] == 0x5555) and np.all(k3[0, 0] == 0x5555)
+
+
 # ---------------------------------------------------------------------------
 # Planted bugs in the append oracle: each must fail at least one pin above.
 # ---------------------------------------------------------------------------
@@ -184,7 +203,7 @@ _PINS = [test_every_finite_code_round_trips, test_midpoints_go_to_even_mantissa,
          lambda: test_append_rebuilds_generated_bf16_cache(gi.LAYOUT_CONTIGUOUS),
          lambda: test_append_rebuilds_generated_bf16_cache(gi.LAYOUT_PAGED),
          test_first_block_append_matches_generator_quantiser, test_later_appends_keep_the_scale_and_clamp,
-         test_append_writes_only_target_rows_paged]
+         test_append_writes_only_target_rows_paged, test_positions_without_a_row_are_not_written]
 
 _orig_encode = A.e4m3fn_encode
 _orig_quantize = A.quantize
