@@ -205,3 +205,35 @@ def test_stress_values(variant):
     kw = dict(v_mean=1.0) if variant == "v_mean1" else dict(q_std=4.0)
     s = spec(h_q=64, h_kv=8, s_q=2, causal=True, fixed_lengths=(3000, 77), **kw)
     check_workload(gi.build(s, seed=31), label=variant)
+
+
+def _many_lengths(batch, seed, hi, long):
+    """Mostly short requests (0 .. hi-1 tokens, empties among them) with a few
+    long ones at given positions."""
+    lens = np.random.default_rng(seed).integers(0, hi, size=batch)
+    for pos, n in long.items():
+        lens[pos] = n
+    return tuple(int(x) for x in lens)
+
+
+@pytest.mark.parametrize("batch", [300, 5000])
+def test_packed_ragged_many_requests(batch):
+    """Thousands of requests in one packed cache: a workgroup's chunk holds
+    hundreds of segments, and finding the first request of a chunk takes two
+    (over 64 requests) or three (over 4096) rounds of the 64-way search."""
+    lens = _many_lengths(batch, batch, 4, {7: 700, batch // 2: 1500, batch - 1: 65})
+    s = spec(layout="ragged", h_q=8, h_kv=2, fixed_lengths=lens)
+    check_workload(gi.build(s, seed=90), label=f"packed, {batch} requests")
+
+
+def test_packed_ragged_max_batch():
+    lens = _many_lengths(65535, 1, 3, {0: 300, 4095: 129, 4096: 1, 40000: 1000, 65534: 33})
+    s = spec(layout="ragged", h_q=4, h_kv=1, head_dim=64, fixed_lengths=lens)
+    check_workload(gi.build(s, seed=91), label="packed, 65535 requests")
+
+
+def test_paged_max_batch():
+    # one workgroup row per request along the grid's third dimension
+    lens = _many_lengths(65535, 2, 33, {0: 32, 65534: 17})
+    s = spec(layout="paged", h_q=4, h_kv=1, head_dim=64, page_size=16, fixed_lengths=lens)
+    check_workload(gi.build(s, seed=92), label="paged, 65535 requests")
