@@ -196,7 +196,14 @@ Tiling plan_tiling(const gqa_decode_params* p, int rows, int math) {
     return t;
   }
   const int loads = p->head_dim * (one_byte(p) ? 1 : 2) / 32;  // per tile and tensor
-  if (loads % 4 == 0) {
+  if (rows > 64 && loads % 8 == 0) {
+    // A head's eight waves (two per SIMD) split the rows: 128 rows with one
+    // block each, 256 with two (d <= 128).
+    t.share = 8;
+    t.hpw = 1;
+    t.mb = (rows > 128 && p->head_dim <= 128) ? 2 : 1;
+    t.row_groups = (int)cdiv(rows, 128 * t.mb);
+  } else if (loads % 4 == 0) {
     t.share = 4;
     t.hpw = 1;
     // One block per wave up to 256 rows (more row groups, two workgroups

@@ -107,8 +107,19 @@ __device__ __forceinline__ int vblk(int blk, int tok) {
 //             number of rows, however the lengths vary.
 constexpr int kDense = 0, kIndirect = 1, kPacked = 2;
 
+// Largest base-2 exponent that a softmax weight may reach before the MFMA
+// path moves its running maximum (weights below 2^8 keep bf16 P and the fp32
+// sums far from overflow).
+constexpr float kLazyRescale = 8.f;
+
+// Waves of a partial workgroup: kPWaves, or eight for row sharing over
+// eight waves (two per SIMD in one workgroup).
+template <int SHARE>
+constexpr int partial_waves() { return SHARE == 8 ? 8 : kPWaves; }
+
+// The launch bound's second value is waves per SIMD.
 template <int D, bool Q8, int MB, int RV, int SHARE>
-constexpr int partial_min_blocks() { return partial_wgs_per_cu(D, Q8, MB, RV, SHARE); }
+constexpr int partial_min_waves() { return partial_wgs_per_cu(D, Q8, MB, RV, SHARE) * partial_waves<SHARE>() / 4; }
 
 // MB: 16-row MFMA blocks (RV = 0).  RV > 0 selects the VALU variant for up
 // to RV query rows (MB = 1): the same loads, LDS staging and pipeline, with
@@ -118,7 +129,7 @@ constexpr int partial_min_blocks() { return partial_wgs_per_cu(D, Q8, MB, RV, SH
 //       lanes of the token completes the score in all of them.
 //   PV: the lane accumulates p x V over its own token slot for its ELT
 //       columns; the token slots are summed once, after the last tile.
-// SHARE = 2 or 4 (row sharing): the SHARE waves of a head split the rows
+// SHARE = 2, 4 or 8 (row sharing): the SHARE waves of a head split the rows
 // instead of the tiles.  Each computes MB 16-row blocks over every tile of
 // the chunk, and each loads and stages 1/SHARE of every tile into a
 // head-wide, double-buffered LDS tile (an LDS-only barrier per tile).  HBM
@@ -127,9 +138,11 @@ constexpr int partial_min_blocks() { return partial_wgs_per_cu(D, Q8, MB, RV, SH
 // (two blocks of d = 256 in one wave do not fit) and for every group of
 // more than 32 rows; a workgroup covers SHARE * MB * 16 rows (row group
 // blockIdx.y / (H_kv / HPW)), and a group of up to 512 rows takes several
-// row groups, each reading the chunk.
+// row groups, each reading the chunk.  SHARE = 8 is a workgroup of eight
+// waves, two per SIMD, for one head: 128 or 256 rows read each tile once,
+// and while one wave of a SIMD runs its softmax the other's MFMAs run.
 template <int D, int KVT, int MODE, int MB, int RV, int SHARE>
-__global__ void __launch_bounds__(kPThreads, (partial_min_blocks<D, KVT != kKvBf16, MB, RV, SHARE>()))
+__global__ void __launch_bounds__(64 * partial_waves<SHARE>(), (partial_min_waves<D, KVT != kKvBf16, MB, RV, SHARE>()))
     gqa_partial_kernel(DecodeArgs a) {
   constexpr bool Q8 = KVT != kKvBf16;          // one-byte codes (FP8 or int8) with scales
   using TS = TileShape<D, Q8>;
@@ -139,8 +152,13 @@ __global__ void __launch_bounds__(kPThreads, (partial_min_blocks<D, KVT != kKvBf
   // Loads per part: a shared tile is loaded in SHARE parts, one per wave.
   constexpr int NLDP = NLD / (SHARED ? SHARE : NPART);
   static_assert(RV == 0 || D <= 128, "the VALU variant is built for d <= 128");
-  static_assert(SHARE == 1 || ((SHARE == 2 || SHARE == 4) && RV == 0 && MB <= 2 && NLD % SHARE == 0),
-                "row sharing: 2 or 4 waves per head, one or two blocks per wave");
+  static_assert(SHARE == 1 || ((SHARE == 2 || SHARE == 4 || SHARE == 8) && RV == 0 && MB <= 2 && NLD % SHARE == 0),
+                "row sharing: 2, 4 or 8 waves per head, one or two blocks per wave");
+  constexpr int NW = partial_waves<SHARE>();    // waves of this workgroup
+  constexpr int NT = 64 * NW;
+  // LDS tiles: one per wave, or two per head (row sharing; eight waves
+  // cover one head)
+  constexpr int NTILE = SHARE == 8 ? 2 : kPWaves;
   constexpr bool INDIRECT = MODE == kIndirect;
   constexpr bool PACKED = MODE == kPacked;
   constexpr bool VALU = RV > 0;
@@ -148,9 +166,13 @@ __global__ void __launch_bounds__(kPThreads, (partial_min_blocks<D, KVT != kKvBf
   constexpr int NR = VALU ? RV : MB;            // running-state rows per lane
   static_assert(!VALU || MB == 1, "the VALU variant computes one block of at most 16 rows");
   static_assert(kPWaves * 16 * D * 4 <= kPWaves * wave_tile_bytes(D, Q8), "accumulators fit in the tiles");
+  // Lazy rescaling (below) keeps a tile's scores live across a branch; the
+  // variants with the most accumulators (four blocks, or two of d = 256)
+  // would spill for it, and rescale at every tile instead.
+  constexpr bool LAZY = MB * D <= 256;
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  __shared__ __attribute__((aligned(16))) unsigned char tiles[kPWaves * wave_tile_bytes(D, Q8)];
+  __shared__ __attribute__((aligned(16))) unsigned char tiles[NTILE * wave_tile_bytes(D, Q8)];
   __shared__ float wstat[2 * kPWaves * 16];
 
   const int lane = threadIdx.x & 63;
@@ -160,7 +182,7 @@ __global__ void __launch_bounds__(kPThreads, (partial_min_blocks<D, KVT != kKvBf
   const int m16 = lane & 15;
   const int qd = lane >> 4;
   const int hpw = a.heads_per_wg;
-  const int wph = kPWaves / hpw;                 // waves per head
+  const int wph = NW / hpw;                      // waves per head
   const int hs = wave % hpw;                    // head slot of this wave
   const int sub = wave / hpw;                   // this wave's share of the head's tiles (or rows)
   const int hgroups = a.h_kv / hpw;             // head groups in grid.y (times the row groups)
@@ -212,7 +234,7 @@ __global__ void __launch_bounds__(kPThreads, (partial_min_blocks<D, KVT != kKvBf
   if constexpr (INDIRECT) {
     // Resolve every slot of the chunk once: physical row and logical token
     // (-1 = masked).  Slots past the end are masked.
-    for (int p = threadIdx.x; p < a.chunk; p += kPThreads) {
+    for (int p = threadIdx.x; p < a.chunk; p += NT) {
       const int pos = start + p;
       int t = -1;
       int64_t row = 0;
@@ -268,6 +290,20 @@ __global__ void __launch_bounds__(kPThreads, (partial_min_blocks<D, KVT != kKvBf
 
   float sc = a.scale_log2;
   if constexpr (Q8) sc *= a.k_scale[b * a.h_kv + g];
+  if constexpr (LAZY && !VALU) {
+    // LAZY variants apply the multiplier inside the exponent (one FMA per
+    // score), which needs it positive: a negative one moves its sign into Q
+    // (exact for bf16), and a zero one (a zero k_scale) becomes the smallest
+    // normal float, which leaves every score zero to within rounding.
+    if (sc < 0.f) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) qop[mb][kk] ^= 0x80008000u;
+      sc = -sc;
+    }
+    sc = fmaxf(sc, 1.17549435e-38f);
+  }
 
   f32x4 acc[VALU ? 1 : MB][NB];
   float accv[VALU ? RV : 1][ELT];
@@ -394,7 +430,7 @@ __global__ void __launch_bounds__(kPThreads, (partial_min_blocks<D, KVT != kKvBf
         f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) c = mfma_16x16x32(kop[kk], qop[mb][kk], c);
-        s[hb][mb] = c * sc;
+        s[hb][mb] = LAZY ? c : c * sc;        // LAZY: unscaled, sc > 0 is applied in the exponent
       }
       if constexpr (D == 256) __builtin_amdgcn_sched_barrier(0);
     }
@@ -425,36 +461,69 @@ __global__ void __launch_bounds__(kPThreads, (partial_min_blocks<D, KVT != kKvBf
 
     // Online softmax (base 2) per query row.  The row sum uses the fp32
     // weights (it sets the LSE); P is rounded to bf16 only as the MFMA
-    // operand of the PV product.
+    // operand of the PV product.  LAZY variants move the running maximum
+    // that the weights are taken against only when a tile's maximum exceeds
+    // it by more than kLazyRescale (base 2): the weights then stay below
+    // 2^kLazyRescale, and most tiles skip the rescale of the accumulators.
+    // Any reference value gives the same O and LSE up to rounding, since l
+    // and O are both taken against it; the decision is made for the whole
+    // wave at once.
     u32x4 pB[MB];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      float mx = fmaxf(fmaxf(fmaxf(s[0][mb][0], s[0][mb][1]), fmaxf(s[0][mb][2], s[0][mb][3])),
-                       fmaxf(fmaxf(s[1][mb][0], s[1][mb][1]), fmaxf(s[1][mb][2], s[1][mb][3])));
-      mx = max_xor32(max_xor16(mx));  // over the four lane groups of the column
-      const float mnew = fmaxf(mrun[mb], mx);
-      const float muse = (mnew == -INFINITY) ? 0.f : mnew;
-      const float alpha = fast_exp2(mrun[mb] - muse);
+    // Weights of one block against the reference -nmuse: fp32 row sum into
+    // lrun, bf16 pairs into pB.
+    auto weights = [&](int mb, float nmuse) __attribute__((always_inline)) {
       float pf[2][4];
       float ps = 0.f;
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          pf[hb][i] = fast_exp2(s[hb][mb][i] - muse);
+          pf[hb][i] = fast_exp2(LAZY ? fmaf(s[hb][mb][i], sc, nmuse) : s[hb][mb][i] + nmuse);
           ps += pf[hb][i];
         }
-      uint32_t pk[4];
+      lrun[mb] += ps;
+      pB[mb] = u32x4{pack_bf16(pf[0][0], pf[0][1]), pack_bf16(pf[0][2], pf[0][3]),
+                     pack_bf16(pf[1][0], pf[1][1]), pack_bf16(pf[1][2], pf[1][3])};
+    };
+    auto tile_max = [&](int mb) __attribute__((always_inline)) -> float {
+      const float mx = fmaxf(fmaxf(fmaxf(s[0][mb][0], s[0][mb][1]), fmaxf(s[0][mb][2], s[0][mb][3])),
+                             fmaxf(fmaxf(s[1][mb][0], s[1][mb][1]), fmaxf(s[1][mb][2], s[1][mb][3])));
+      const float m = max_xor32(max_xor16(mx));  // over the four lane groups of the column
+      return LAZY ? m * sc : m;
+    };
+    if constexpr (LAZY) {
+      float mt[MB];
+      bool grow = false;
 #pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        pk[2 * hb] = pack_bf16(pf[hb][0], pf[hb][1]);
-        pk[2 * hb + 1] = pack_bf16(pf[hb][2], pf[hb][3]);
+      for (int mb = 0; mb < MB; ++mb) {
+        mt[mb] = tile_max(mb);
+        grow |= mt[mb] > mrun[mb] + kLazyRescale;
       }
-      lrun[mb] = lrun[mb] * alpha + ps;
-      mrun[mb] = mnew;
-      pB[mb] = u32x4{pk[0], pk[1], pk[2], pk[3]};
+      if (__any(grow)) {
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) acc[mb][nb] *= alpha;
+        for (int mb = 0; mb < MB; ++mb) {
+          const float mnew = fmaxf(mrun[mb], mt[mb]);
+          const float alpha = fast_exp2(mrun[mb] - (mnew == -INFINITY ? 0.f : mnew));
+          lrun[mb] *= alpha;
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) acc[mb][nb] *= alpha;
+          mrun[mb] = mnew;
+        }
+      }
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) weights(mb, mrun[mb] == -INFINITY ? 0.f : -mrun[mb]);
+    } else {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const float mnew = fmaxf(mrun[mb], tile_max(mb));
+        const float muse = (mnew == -INFINITY) ? 0.f : mnew;
+        const float alpha = fast_exp2(mrun[mb] - muse);
+        lrun[mb] *= alpha;
+        mrun[mb] = mnew;
+        weights(mb, -muse);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[mb][nb] *= alpha;
+      }
     }
 
     // V^T operand: lane (m16, qd) needs column d = 16 nb + m16 for tokens
@@ -1055,8 +1124,8 @@ template <int D, int KVT, int MODE, int MB, int RV, int SHARE = 1>
 static hipError_t launch_partial_t(const DecodeArgs& a, dim3 grid, hipStream_t st, hipEvent_t ev0,
                                    hipEvent_t ev1) {
   const size_t lds = table_bytes(MODE == kIndirect, a.chunk);
-  hipExtLaunchKernelGGL((gqa_partial_kernel<D, KVT, MODE, MB, RV, SHARE>), grid, dim3(kPThreads), lds, st, ev0, ev1, 0,
-                        a);
+  hipExtLaunchKernelGGL((gqa_partial_kernel<D, KVT, MODE, MB, RV, SHARE>), grid, dim3(64 * partial_waves<SHARE>()),
+                        lds, st, ev0, ev1, 0, a);
   return hipGetLastError();
 }
 
@@ -1077,6 +1146,13 @@ static hipError_t launch_mb(const DecodeArgs& a, int mb, int rv, int share, dim3
     if constexpr (NLD % 4 == 0) {
       if (mb == 1) return launch_partial_t<D, KVT, MODE, 1, 0, 4>(a, grid, st, ev0, ev1);
       if constexpr (D <= 128) return launch_partial_t<D, KVT, MODE, 2, 0, 4>(a, grid, st, ev0, ev1);
+    }
+    return hipErrorInvalidValue;
+  }
+  if (share == 8) {
+    if constexpr (NLD % 8 == 0) {
+      if (mb == 1) return launch_partial_t<D, KVT, MODE, 1, 0, 8>(a, grid, st, ev0, ev1);
+      if constexpr (D <= 128) return launch_partial_t<D, KVT, MODE, 2, 0, 8>(a, grid, st, ev0, ev1);
     }
     return hipErrorInvalidValue;
   }
