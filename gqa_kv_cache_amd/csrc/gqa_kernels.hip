@@ -165,7 +165,11 @@ __global__ void __launch_bounds__(64 * partial_waves<SHARE>(), (partial_min_wave
   constexpr int ELT = Q8 ? 16 : 8;             // elements of one 16-byte chunk
   constexpr int NR = VALU ? RV : MB;            // running-state rows per lane
   static_assert(!VALU || MB == 1, "the VALU variant computes one block of at most 16 rows");
-  static_assert(kPWaves * 16 * D * 4 <= kPWaves * wave_tile_bytes(D, Q8), "accumulators fit in the tiles");
+  // Row stride (floats) of the accumulators the waves of a head merge
+  // through LDS after the tile loop: four floats of padding put the 16 rows
+  // one store covers on different banks.
+  constexpr int WST = D + 4;
+  static_assert(kPWaves * 16 * WST * 4 <= kPWaves * wave_tile_bytes(D, Q8), "accumulators fit in the tiles");
   // Lazy rescaling (below) keeps a tile's scores live across a branch; the
   // variants with the most accumulators (four blocks, or two of d = 256)
   // would spill for it, and rescale at every tile instead.
@@ -804,10 +808,13 @@ __global__ void __launch_bounds__(64 * partial_waves<SHARE>(), (partial_min_wave
     for (int mb = 0; mb < MB; ++mb) lrun[mb] = sum_xor32(sum_xor16(lrun[mb]));
   }
 
-  if constexpr (SHARED) {
+  if (SHARED || (!VALU && LAZY && wph == 1)) {
     // Each wave holds complete rows (MB blocks of 16 of its head's group):
-    // normalise and write them from registers.  Lane (m16, qd) of block mb
-    // has row rbase + 16 mb + m16, columns 16 nb + 4 qd .. +3.
+    // with rows shared, or with one wave per head (HPW = 4), no merge is
+    // needed (the variants with the most accumulators keep the merge, whose
+    // code they are built around).  Normalise and write them from
+    // registers.  Lane (m16, qd) of block mb has row rbase + 16 mb + m16,
+    // columns 16 nb + 4 qd .. +3.
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       const int r = rbase + mb * 16 + m16;
@@ -875,7 +882,7 @@ __global__ void __launch_bounds__(64 * partial_waves<SHARE>(), (partial_min_wave
           for (int r = 0; r < RV; ++r)
 #pragma unroll
             for (int e = 0; e < ELT; e += 4)
-              *reinterpret_cast<f32x4*>(wacc + (wave * 16 + r) * D + ELT * lch + e) =
+              *reinterpret_cast<f32x4*>(wacc + (wave * 16 + r) * WST + ELT * lch + e) =
                   f32x4{accv[r][e], accv[r][e + 1], accv[r][e + 2], accv[r][e + 3]};
         }
       } else {
@@ -885,7 +892,7 @@ __global__ void __launch_bounds__(64 * partial_waves<SHARE>(), (partial_min_wave
         }
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
-          *reinterpret_cast<f32x4*>(wacc + (wave * 16 + m16) * D + 16 * nb + 4 * qd) = acc[mb][nb];
+          *reinterpret_cast<f32x4*>(wacc + (wave * 16 + m16) * WST + 16 * nb + 4 * qd) = acc[mb][nb];
       }
       __syncthreads();
 
@@ -909,7 +916,7 @@ __global__ void __launch_bounds__(64 * partial_waves<SHARE>(), (partial_min_wave
             const int w = hh + k * hpw;
             const float e = fast_exp2(wm[w * 16 + rl] - M);
             sum += e * wl[w * 16 + rl];
-            const float* src = wacc + (w * 16 + rl) * D + d8 * 8;
+            const float* src = wacc + (w * 16 + rl) * WST + d8 * 8;
             const f32x4 x0 = *reinterpret_cast<const f32x4*>(src);
             const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + 4);
 #pragma unroll
