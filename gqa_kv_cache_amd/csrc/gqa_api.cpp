@@ -90,8 +90,6 @@ gqa_status check_shape(const gqa_decode_params* p) {
   const int64_t rows = (int64_t)(p->h_q / p->h_kv) * p->s_q;
   if (rows > kMaxRows)
     return fail(GQA_ERR_UNSUPPORTED, "(h_q/h_kv)*s_q = %lld query rows per KV head exceeds %d", (long long)rows, kMaxRows);
-  if (rows > 64 && p->kv_dtype != GQA_KV_BF16 && p->head_dim == 64 && p->h_kv % 2 != 0)
-    return fail(GQA_ERR_UNSUPPORTED, "more than 64 rows per KV head with one-byte codes at d = 64 needs an even h_kv");
   if (p->layout < GQA_LAYOUT_CONTIGUOUS || p->layout > GQA_LAYOUT_PAGED)
     return fail(GQA_ERR_INVALID_ARG, "unknown layout %d", p->layout);
   if (p->kv_dtype != GQA_KV_BF16 && p->kv_dtype != GQA_KV_FP8_E4M3FN && p->kv_dtype != GQA_KV_INT8)
@@ -177,11 +175,23 @@ static_assert(gqa::kPWaves == 4, "row sharing is laid out for 4 waves per workgr
 // Up to 16 rows: one block per wave, the waves of a head taking alternate
 // tiles.  17-32 rows: two blocks per wave, except d = 256 (two blocks of
 // d = 256 do not fit a wave's registers), where a head's two waves split
-// the rows and share the tiles through LDS (even H_kv).  More than 32 rows:
-// a head's four waves split the rows, one block each up to 256 rows, two
-// (d <= 128) beyond, and groups of more rows than one workgroup covers
-// take several row groups.  FP8 d = 64 tiles are two loads per tensor, so
-// there two waves per head split the rows, two blocks each.
+// the rows and share the tiles through LDS (even H_kv).  33-64 rows: a
+// head's four waves split the rows, one block each (FP8 and int8 at d = 64,
+// whose tiles are two loads per tensor: two waves per head, two blocks
+// each, or one wave of four blocks for odd H_kv).  More rows: a workgroup
+// of eight waves per head, one block each up to 128 rows and two beyond
+// (d <= 128), and groups of more rows than one workgroup covers take
+// several row groups (four-wave row groups of 64 for bf16 d = 64 up to 256
+// rows, below).  MI355X, one process, us per call against four
+// waves per head (one block each, row groups of 64): 512 rows 653 -> 351
+// (bf16 d = 128, 128K) and 638 -> 383 (FP8); 128 rows 47.5 -> 42.6 (bf16
+// d = 128, 4 x 32K) and 230 -> 204 (FP8, 8 x 32K).  The exception is bf16
+// at d = 64 up to 256 rows: only four of the eight waves load its tiles,
+// and four waves per head in two workgroups per CU keep twice the bytes in
+// flight.  Measured there: 160 rows (80/1, 128K) 27.9 with four waves
+// against 30.3 us, 128 rows 30.8 against 34.2 us (16/2, 4 x 32K) but 160
+// against 147 us (64/8, 8 x 32K); at 512 rows (8/1, 128K) eight waves win,
+// 55.6 -> 47.3 us.
 Tiling plan_tiling(const gqa_decode_params* p, int rows, int math) {
   Tiling t;
   t.hpw = heads_per_wg(p->h_kv);
@@ -196,9 +206,8 @@ Tiling plan_tiling(const gqa_decode_params* p, int rows, int math) {
     return t;
   }
   const int loads = p->head_dim * (one_byte(p) ? 1 : 2) / 32;  // per tile and tensor
-  if (rows > 64 && loads % 8 == 0) {
-    // A head's eight waves (two per SIMD) split the rows: 128 rows with one
-    // block each, 256 with two (d <= 128).
+  const bool bf16_d64 = !one_byte(p) && p->head_dim == 64;
+  if (rows > 64 && !(bf16_d64 && rows <= 256)) {
     t.share = 8;
     t.hpw = 1;
     t.mb = (rows > 128 && p->head_dim <= 128) ? 2 : 1;
@@ -206,13 +215,7 @@ Tiling plan_tiling(const gqa_decode_params* p, int rows, int math) {
   } else if (loads % 4 == 0) {
     t.share = 4;
     t.hpw = 1;
-    // One block per wave up to 256 rows (more row groups, two workgroups
-    // per CU), two beyond (d <= 128), where the row groups' repeated reads
-    // of the chunk cost more than the extra residency gains.  MI355X, one
-    // process: 128 rows 93.6 -> 81.5 us and 256 rows 325 -> 287 us with one
-    // block; 512 rows 643 us with two against 783 us with one.
-    t.mb = (rows > 256 && p->head_dim <= 128) ? 2 : 1;
-    t.row_groups = (int)cdiv(rows, 64 * t.mb);
+    t.row_groups = (int)cdiv(rows, 64);
   } else if (p->h_kv % 2 == 0) {
     t.share = 2;
     t.hpw = 2;

@@ -41,7 +41,10 @@ constexpr int kPWaves = GQA_PARTIAL_WAVES;
 // in flight.  The VALU variant keeps RV x (8 or 16) fp32 accumulators and
 // every score of a tile per lane, and also takes the whole file.
 __host__ __device__ constexpr int partial_wgs_per_cu(int D, bool fp8, int mb, int rv, int share) {
-  return (rv == 0 && mb == 1 && ((share == 1 && (fp8 || D == 64)) || (share == 4 && D <= 128))) ? 2 : 1;
+  return (rv == 0 && mb == 1 &&
+          ((share == 1 && (fp8 || D == 64)) || (share == 4 && D <= 128) || (share == 8 && (fp8 || D == 64))))
+             ? 2
+             : 1;
 }
 constexpr int kPThreads = 64 * kPWaves;
 

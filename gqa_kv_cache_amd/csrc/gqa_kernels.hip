@@ -149,10 +149,14 @@ __global__ void __launch_bounds__(64 * partial_waves<SHARE>(), (partial_min_wave
   constexpr int RB = TS::RB, CPR = TS::CPR, TPI = TS::TPI, NLD = TS::NLD, KK = TS::KK, NB = TS::NB;
   constexpr bool SHARED = SHARE > 1;
   constexpr int NPART = TS::NPART;
-  // Loads per part: a shared tile is loaded in SHARE parts, one per wave.
-  constexpr int NLDP = NLD / (SHARED ? SHARE : NPART);
+  // Loads per part: a shared tile is loaded in SHARE parts, one per wave;
+  // with fewer loads per tile than waves (eight waves over one-byte or
+  // d = 64 tiles), the first NLD waves load one each and the rest none.
+  constexpr int NLDP = SHARED ? (NLD >= SHARE ? NLD / SHARE : 1) : NLD / NPART;
+  constexpr int NLOADERS = SHARED ? NLD / NLDP : 1;
   static_assert(RV == 0 || D <= 128, "the VALU variant is built for d <= 128");
-  static_assert(SHARE == 1 || ((SHARE == 2 || SHARE == 4 || SHARE == 8) && RV == 0 && MB <= 2 && NLD % SHARE == 0),
+  static_assert(SHARE == 1 || ((SHARE == 2 || SHARE == 4 || SHARE == 8) && RV == 0 && MB <= 2 &&
+                                (NLD % SHARE == 0 || SHARE % NLD == 0)),
                 "row sharing: 2, 4 or 8 waves per head, one or two blocks per wave");
   constexpr int NW = partial_waves<SHARE>();    // waves of this workgroup
   constexpr int NT = 64 * NW;
@@ -358,6 +362,7 @@ __global__ void __launch_bounds__(64 * partial_waves<SHARE>(), (partial_min_wave
   // 16-byte location with every lane: no branch, no HBM traffic to speak of.
   auto load_tile = [&](int tile, u32x4 (&kr)[NLDP], u32x4 (&vr)[NLDP], bool real, int part = 0)
       __attribute__((always_inline)) {
+    if (NLOADERS < SHARE && part >= NLOADERS) return;   // a wave with no part of the tile
     const int tb = start + tile * kTile;
     const int lane_on = real ? 1 : 0;
 #pragma unroll
@@ -374,7 +379,7 @@ __global__ void __launch_bounds__(64 * partial_waves<SHARE>(), (partial_min_wave
   auto stage_tile = [&](const u32x4 (&kr)[NLDP], const u32x4 (&vr)[NLDP], int part = 0)
       __attribute__((always_inline)) {
 #pragma unroll
-    for (int ii = 0; ii < NLDP; ++ii) {
+    for (int ii = 0; ii < ((NLOADERS < SHARE && part >= NLOADERS) ? 0 : NLDP); ++ii) {
       const int i = part * NLDP + ii;
       const int tok = i * TPI + ltok;
       kt[tok * CPR + kchunk<CPR>(lch, tok)] = kr[ii];
@@ -1157,10 +1162,8 @@ static hipError_t launch_mb(const DecodeArgs& a, int mb, int rv, int share, dim3
     return hipErrorInvalidValue;
   }
   if (share == 8) {
-    if constexpr (NLD % 8 == 0) {
-      if (mb == 1) return launch_partial_t<D, KVT, MODE, 1, 0, 8>(a, grid, st, ev0, ev1);
-      if constexpr (D <= 128) return launch_partial_t<D, KVT, MODE, 2, 0, 8>(a, grid, st, ev0, ev1);
-    }
+    if (mb == 1) return launch_partial_t<D, KVT, MODE, 1, 0, 8>(a, grid, st, ev0, ev1);
+    if constexpr (D <= 128) return launch_partial_t<D, KVT, MODE, 2, 0, 8>(a, grid, st, ev0, ev1);
     return hipErrorInvalidValue;
   }
   if constexpr (D <= 128) {

@@ -69,7 +69,6 @@ BAD_SHAPES = [
     (dict(head_dim=256, math="valu"), 2),         # the VALU path is built for d <= 128
     (dict(h_q=1024, h_kv=1), 2),            # 1024 rows per KV head
     (dict(h_q=16, h_kv=1, s_q=64), 2),      # 1024 rows
-    (dict(h_q=80, h_kv=1, kv_dtype="fp8_e4m3fn", head_dim=64), 2),   # FP8 d64, > 64 rows, odd H_kv
     (dict(layout=7), 1),
     (dict(kv_dtype=3), 1),
     (dict(gate_mode=5), 1),
@@ -239,18 +238,27 @@ def test_append_batch_zero_is_a_no_op():
 
 
 def test_plan_tiling_of_large_groups():
-    # rows -> 16-row blocks per KV head: one block per wave of four in row
-    # groups of 64 up to 256 rows; beyond, two blocks per wave (d <= 128) in
-    # row groups of 128
+    # rows -> 16-row blocks per KV head: four waves of one block up to 64
+    # rows; beyond, eight waves of one block (128 rows per row group) or of
+    # two (d <= 128, more than 128 rows: 256 per row group); bf16 at d = 64
+    # keeps four waves (row groups of 64) up to 256 rows
     def plan(**kw):
         d = dict(batch=1, s_q=1, h_q=8, h_kv=8, head_dim=128, max_seqlen_kv=4096, seq_capacity=4096,
                  kv_rows=4096, num_cus=256)
         d.update(kw)
         return G.gqa_decode_make_plan(G.make_params(**d))
     assert plan(h_q=48, h_kv=1)["row_blocks"] == 4                       # 48 rows: 4 waves x 1 block
-    assert plan(h_q=64, h_kv=8, s_q=16)["row_blocks"] == 8               # 128 rows: 4 x 1, two row groups
-    assert plan(h_q=64, h_kv=8, s_q=64)["row_blocks"] == 32              # 512 rows: 4 row groups of 128
-    assert plan(h_q=64, h_kv=8, s_q=64, head_dim=256)["row_blocks"] == 32  # d256: 8 groups of 64
+    assert plan(h_q=64, h_kv=8, s_q=16)["row_blocks"] == 8               # 128 rows: 8 waves x 1
+    assert plan(h_q=96, h_kv=1)["row_blocks"] == 8                       # 96 rows: 8 x 1, 2 blocks idle
+    assert plan(h_q=64, h_kv=8, s_q=64)["row_blocks"] == 32              # 512 rows: 2 row groups of 8 x 2
+    assert plan(h_q=64, h_kv=8, s_q=64, head_dim=256)["row_blocks"] == 32  # d256: 4 row groups of 8 x 1
     assert plan(h_q=32, h_kv=2, s_q=2, head_dim=256)["row_blocks"] == 2  # two waves x 1 block
+    assert plan(h_q=64, h_kv=8, s_q=16, head_dim=64)["row_blocks"] == 8  # bf16 d64, 128 rows: 2 x (4 x 1)
+    assert plan(h_q=80, h_kv=1, s_q=2, head_dim=64)["row_blocks"] == 12  # bf16 d64, 160 rows: 3 x (4 x 1)
+    assert plan(h_q=64, h_kv=1, s_q=8, head_dim=64)["row_blocks"] == 32  # bf16 d64, 512 rows: 2 x (8 x 2)
+    fp8_d64 = dict(head_dim=64, kv_dtype="fp8_e4m3fn")
+    assert plan(h_q=80, h_kv=1, **fp8_d64)["row_blocks"] == 8            # 80 rows, odd H_kv: 8 x 1
+    assert plan(h_q=48, h_kv=1, **fp8_d64)["row_blocks"] == 4            # 48 rows, odd H_kv: 1 wave x 4
+    assert plan(h_q=96, h_kv=2, **fp8_d64)["row_blocks"] == 4            # 48 rows, even H_kv: 2 waves x 2
     p1, p4 = plan(h_q=64, h_kv=8, s_q=2), plan(h_q=64, h_kv=8, s_q=64)
     assert p4["partial_workgroups"] >= p1["partial_workgroups"]

@@ -100,3 +100,33 @@ def test_large_sq_query_block_longer_than_cache():
     # S_q larger than n: the first S_q - n queries see nothing (O = 0, LSE = -inf)
     s = spec(h_q=8, h_kv=2, s_q=64, fixed_lengths=(20, 64, 1))
     check_workload(gi.build(s, seed=901), label="S_q=64 over short caches")
+
+
+# Eight waves over tiles of fewer than eight loads per tensor (FP8 and int8,
+# bf16 at d 64 beyond 256 rows): the first four or two waves load and stage
+# each tile, and all eight compute on it.
+SMALL_TILES = [
+    # (kv_dtype, h_q, h_kv, s_q, d)
+    (gi.KV_FP8, 32, 2, 16, 128),    # 256 rows: two blocks per wave, four loading waves
+    (gi.KV_INT8, 16, 2, 16, 128),   # 128 rows: one block per wave
+    (gi.KV_FP8, 80, 1, 2, 64),      # 160 rows, odd H_kv: two loading waves
+    (gi.KV_INT8, 40, 1, 8, 64),     # 320 rows: two row groups of 256
+    (gi.KV_BF16, 40, 1, 8, 64),     # 320 rows, bf16 d 64: eight waves, two row groups
+    (gi.KV_BF16, 80, 1, 2, 64),     # 160 rows, bf16 d 64: four waves, three row groups
+    (gi.KV_FP8, 16, 1, 16, 256),    # 256 rows, d 256: two row groups of 128
+]
+
+
+@pytest.mark.parametrize("kvd,hq,hkv,sq,d", SMALL_TILES)
+def test_large_sq_small_tiles(kvd, hq, hkv, sq, d):
+    s = spec(h_q=hq, h_kv=hkv, s_q=sq, head_dim=d, kv_dtype=kvd, gate=kvd != gi.KV_BF16,
+             fixed_lengths=(700, sq, sq + 37))
+    check_workload(gi.build(s, seed=1000 + hq + sq + d), label=f"{kvd} {hq}/{hkv} S_q={sq} d={d}")
+
+
+@pytest.mark.parametrize("layout", ["ragged", "paged"])
+@pytest.mark.parametrize("kvd", [gi.KV_FP8, gi.KV_INT8])
+def test_large_sq_small_tiles_layouts(layout, kvd):
+    s = spec(layout=layout, h_q=64, h_kv=4, s_q=8, head_dim=128, kv_dtype=kvd, gate=True, page_size=16,
+             fixed_lengths=(333, 8, 1000, 0, 65))
+    check_workload(gi.build(s, seed=1100), gate_mode="headwise", label=f"{kvd} {layout} 128 rows")
