@@ -185,7 +185,7 @@ static_assert(gqa::kPWaves == 4, "row sharing is laid out for 4 waves per workgr
 // rows, below).  MI355X, one process, us per call against four
 // waves per head (one block each, row groups of 64): 512 rows 653 -> 351
 // (bf16 d = 128, 128K) and 638 -> 383 (FP8); 128 rows 47.5 -> 42.6 (bf16
-// d = 128, 4 x 32K) and 230 -> 204 (FP8, 8 x 32K).  The exception is bf16
+// d = 128, 4 x 32K) and 229 -> 206 (FP8, 8 x 32K).  The exception is bf16
 // at d = 64 up to 256 rows: only four of the eight waves load its tiles,
 // and four waves per head in two workgroups per CU keep twice the bytes in
 // flight.  Measured there: 160 rows (80/1, 128K) 27.9 with four waves
