@@ -33,9 +33,12 @@ constexpr int kPWaves = GQA_PARTIAL_WAVES;
 
 // Resident partial workgroups per CU that a kernel variant's register
 // budget is built for (its launch bounds), and that the planner sizes the
-// grid for.  Two for one 16-row block of FP8 or d = 64 tiles, and for the
-// row-sharing variants with one block per wave at d <= 128; one (the whole
-// register file) for bf16 d = 128 with the waves splitting the tiles, whose
+// grid for.  Two for one 16-row block of FP8 or d = 64 tiles, for the
+// four-wave row-sharing variants with one block per wave at d <= 128, and
+// for the eight-wave ones with one block per wave over one-byte or d = 64
+// tiles (four waves per SIMD in 128 VGPRs each); one (the whole register
+// file, or half of it for eight waves) otherwise: for bf16 d = 128 with the
+// waves splitting the tiles, whose
 // two register buffers of whole-row loads alone take 128 VGPRs -- squeezed
 // into half the file it spills, and every spill reload waits for all loads
 // in flight.  The VALU variant keeps RV x (8 or 16) fp32 accumulators and

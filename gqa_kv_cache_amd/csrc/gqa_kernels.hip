@@ -6,7 +6,10 @@
 // share a head take alternate 32-position tiles of the chunk and are merged
 // in LDS at the end.  With HPW = 4 the workgroup reads, for every token, a
 // contiguous 1 KiB of the cache (four heads' K or V), which is what lets
-// HBM run close to its streaming rate.
+// HBM run close to its streaming rate.  Groups of more than 16 query rows
+// per KV head can instead split the rows over the waves of a head (two,
+// four, or eight in a workgroup of 8 wave64s), which share each tile
+// through LDS (SHARE below).
 //
 // Each K/V tile of a head is loaded from HBM once and serves every query row
 // of the head's group: G = H_q / H_kv query heads times S_q query tokens,
