@@ -2,11 +2,12 @@
 verification): 17 to 512 query rows per KV head, against the fp64 oracle
 (needs a gfx950 GPU).
 
-These rows are laid over a KV head's four waves, which split the rows and
-share every tile through LDS (one or two 16-row blocks each), and over
+These rows are laid over a KV head's two, four or eight waves, which split
+the rows and share every tile through LDS (one or two 16-row blocks each;
+with eight waves over small tiles only the first waves load), and over
 several row groups when a group has more rows than a workgroup covers.
-The cases cross every such tiling with the cache layouts, FP8 and the
-gates, forced splits, and the causal alignment of the query block.
+The cases cross every such tiling with the cache layouts, FP8, int8 and
+the gates, forced splits, and the causal alignment of the query block.
 """
 
 import numpy as np
@@ -32,16 +33,16 @@ SHAPES = [
     (4, 2, 16, 128),    # 32 rows: two blocks in one wave
     (6, 2, 16, 128),    # 48 rows: four waves, one block each
     (8, 2, 16, 128),    # 64 rows
-    (10, 2, 13, 128),   # 65 rows: four waves, one block each, two row groups
-    (16, 2, 16, 128),   # 128 rows: two row groups
-    (18, 2, 16, 128),   # 144 rows: three row groups
-    (64, 8, 64, 128),   # 512 rows: two blocks per wave, four row groups
+    (10, 2, 13, 128),   # 65 rows: eight waves, one block each
+    (16, 2, 16, 128),   # 128 rows
+    (18, 2, 16, 128),   # 144 rows: eight waves of two blocks
+    (64, 8, 64, 128),   # 512 rows: two row groups of 256
     (8, 1, 64, 64),     # 512 rows, d 64
     (8, 8, 16, 64),     # 16 rows, d 64
     (12, 4, 16, 64),    # 48 rows, d 64
     (6, 2, 16, 256),    # 48 rows, d 256: four waves, one block each
-    (16, 2, 16, 256),   # 128 rows, d 256: two row groups of 64
-    (64, 8, 64, 256),   # 512 rows, d 256: eight row groups
+    (16, 2, 16, 256),   # 128 rows, d 256: eight waves, one block each
+    (64, 8, 64, 256),   # 512 rows, d 256: four row groups of 128
 ]
 
 
