@@ -35,17 +35,17 @@ constexpr int kPWaves = GQA_PARTIAL_WAVES;
 // budget is built for (its launch bounds), and that the planner sizes the
 // grid for.  Two for one 16-row block of FP8 or d = 64 tiles, for the
 // four-wave row-sharing variants with one block per wave at d <= 128, and
-// for the eight-wave ones with one block per wave over one-byte or d = 64
-// tiles (four waves per SIMD in 128 VGPRs each); one (the whole register
-// file, or half of it for eight waves) otherwise: for bf16 d = 128 with the
-// waves splitting the tiles, whose
+// for the eight-wave ones with one block per wave at d = 64 (four waves per
+// SIMD in 128 VGPRs each; at d = 128 and 256 those spill); one (the whole
+// register file, or half of it for eight waves) otherwise: for bf16
+// d = 128 with the waves splitting the tiles, whose
 // two register buffers of whole-row loads alone take 128 VGPRs -- squeezed
 // into half the file it spills, and every spill reload waits for all loads
 // in flight.  The VALU variant keeps RV x (8 or 16) fp32 accumulators and
 // every score of a tile per lane, and also takes the whole file.
 __host__ __device__ constexpr int partial_wgs_per_cu(int D, bool fp8, int mb, int rv, int share) {
   return (rv == 0 && mb == 1 &&
-          ((share == 1 && (fp8 || D == 64)) || (share == 4 && D <= 128) || (share == 8 && (fp8 || D == 64))))
+          ((share == 1 && (fp8 || D == 64)) || (share == 4 && D <= 128) || (share == 8 && D == 64)))
              ? 2
              : 1;
 }

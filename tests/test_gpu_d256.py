@@ -102,14 +102,22 @@ def test_d256_one_hot_rows(chunk):
     log(f"  d256 one-hot chunk={chunk}: exact")
 
 
-# 17 to 32 rows with an even H_kv: the two waves of a head take one 16-row
-# block each and share every tile through LDS.  Odd H_kv keeps two blocks
-# in one wave.
+# 17 to 32 rows: bf16 takes eight waves per head (the first two with rows,
+# all eight loading the tiles); FP8 and int8 with an even H_kv the two waves
+# of a head, one 16-row block each, sharing every tile through LDS; with an
+# odd H_kv two blocks in one wave.
 @pytest.mark.parametrize("hq,hkv,sq", [(24, 1, 1), (48, 2, 1), (16, 2, 3), (20, 4, 4), (34, 2, 1), (32, 1, 1),
                                        (96, 3, 1)])
 def test_d256_shared_rows_dense(hq, hkv, sq):
     s = spec(h_q=hq, h_kv=hkv, s_q=sq, causal=sq > 1, fixed_lengths=(1500, 33, 1))
     check_workload(gi.build(s, seed=800 + hq + hkv + sq), label=f"d256 shared {hq}/{hkv} S_q={sq}")
+
+
+@pytest.mark.parametrize("kvd", [gi.KV_FP8, gi.KV_INT8])
+@pytest.mark.parametrize("hq,hkv,sq", [(48, 2, 1), (24, 1, 1), (16, 2, 3)])
+def test_d256_17_to_32_rows_one_byte(kvd, hq, hkv, sq):
+    s = spec(h_q=hq, h_kv=hkv, s_q=sq, causal=sq > 1, kv_dtype=kvd, gate=True, fixed_lengths=(1200, 40, 1))
+    check_workload(gi.build(s, seed=850 + hq + hkv + sq), label=f"d256 {kvd} {hq}/{hkv} S_q={sq}")
 
 
 @pytest.mark.parametrize("layout,chunk", [("ragged", 0), ("ragged", 64), ("paged", 0), ("paged", 32),
