@@ -174,12 +174,12 @@ static_assert(gqa::kPWaves == 4, "row sharing is laid out for 4 waves per workgr
 
 // Up to 16 rows: one block per wave, the waves of a head taking alternate
 // tiles.  17-32 rows: two blocks per wave, except d = 256 (two blocks of
-// d = 256 do not fit a wave's registers).  There bf16 takes eight waves per
-// head (two of them with rows; all eight load and stage the tiles, which
-// keeps more of them in flight: 62.0 -> 55.6 us for 32/2 heads at 128K
-// against two waves per head), and FP8 or int8 with an even H_kv a head's
-// two waves, which split the rows and share the tiles through LDS (eight
-// waves measured 54.7 against 45.9 us there).  33-64 rows: a
+// d = 256 do not fit a wave's registers), where a head's two waves split
+// the rows and share the tiles through LDS (even H_kv).  Eight waves per
+// head there (two with rows, all eight loading) ran the partial kernel
+// faster for bf16 (54.3 against 55.8 us, 32/2 heads at 128K) but the whole
+// call slower in back-to-back calls (64.7 against 63.3 us), and FP8 slower
+// (54.7 against 45.9 us); they are not used.  33-64 rows: a
 // head's four waves split the rows, one block each (FP8 and int8 at d = 64,
 // whose tiles are two loads per tensor: two waves per head, two blocks
 // each, or one wave of four blocks for odd H_kv).  More rows: a workgroup
@@ -201,10 +201,7 @@ Tiling plan_tiling(const gqa_decode_params* p, int rows, int math) {
   t.hpw = heads_per_wg(p->h_kv);
   if (math == GQA_MATH_VALU || rows <= 16) return t;
   if (rows <= 32) {
-    if (p->head_dim == 256 && !one_byte(p)) {
-      t.share = 8;
-      t.hpw = 1;
-    } else if (p->head_dim == 256 && p->h_kv % 2 == 0) {
+    if (p->head_dim == 256 && p->h_kv % 2 == 0) {
       t.share = 2;
       t.hpw = 2;
     } else {

@@ -252,8 +252,8 @@ def test_plan_tiling_of_large_groups():
     assert plan(h_q=96, h_kv=1)["row_blocks"] == 8                       # 96 rows: 8 x 1, 2 blocks idle
     assert plan(h_q=64, h_kv=8, s_q=64)["row_blocks"] == 32              # 512 rows: 2 row groups of 8 x 2
     assert plan(h_q=64, h_kv=8, s_q=64, head_dim=256)["row_blocks"] == 32  # d256: 4 row groups of 8 x 1
-    assert plan(h_q=32, h_kv=2, s_q=2, head_dim=256)["row_blocks"] == 8  # 32 rows: 8 waves x 1 (6 idle)
-    assert plan(h_q=32, h_kv=2, s_q=2, head_dim=256, kv_dtype="fp8_e4m3fn")["row_blocks"] == 2  # 2 waves x 1
+    assert plan(h_q=32, h_kv=2, s_q=2, head_dim=256)["row_blocks"] == 2  # two waves x 1 block
+    assert plan(h_q=32, h_kv=2, s_q=2, head_dim=256, kv_dtype="fp8_e4m3fn")["row_blocks"] == 2
     assert plan(h_q=64, h_kv=8, s_q=16, head_dim=64)["row_blocks"] == 8  # bf16 d64, 128 rows: 2 x (4 x 1)
     assert plan(h_q=80, h_kv=1, s_q=2, head_dim=64)["row_blocks"] == 12  # bf16 d64, 160 rows: 3 x (4 x 1)
     assert plan(h_q=64, h_kv=1, s_q=8, head_dim=64)["row_blocks"] == 32  # bf16 d64, 512 rows: 2 x (8 x 2)

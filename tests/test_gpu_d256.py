@@ -102,10 +102,9 @@ def test_d256_one_hot_rows(chunk):
     log(f"  d256 one-hot chunk={chunk}: exact")
 
 
-# 17 to 32 rows: bf16 takes eight waves per head (the first two with rows,
-# all eight loading the tiles); FP8 and int8 with an even H_kv the two waves
-# of a head, one 16-row block each, sharing every tile through LDS; with an
-# odd H_kv two blocks in one wave.
+# 17 to 32 rows with an even H_kv: the two waves of a head take one 16-row
+# block each and share every tile through LDS.  Odd H_kv keeps two blocks
+# in one wave.
 @pytest.mark.parametrize("hq,hkv,sq", [(24, 1, 1), (48, 2, 1), (16, 2, 3), (20, 4, 4), (34, 2, 1), (32, 1, 1),
                                        (96, 3, 1)])
 def test_d256_shared_rows_dense(hq, hkv, sq):
