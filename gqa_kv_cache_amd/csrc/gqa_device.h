@@ -251,17 +251,15 @@ __device__ __forceinline__ void fp8x4_to_bf16x4(uint32_t w, uint32_t& lo, uint32
 }
 
 // Four int8 codes (one dword, lowest byte first) -> four bf16 in two dwords.
-// Every int8 value is exactly representable in bf16: bias each byte by 128
-// (x ^ 0x80 = x + 128 as an unsigned byte), convert it with
-// v_cvt_f32_ubyte, subtract 128 (exact), and keep the upper halves of the
-// fp32 results (exact: at most 8 significant bits).
+// Every int8 value is exactly representable in bf16: convert each
+// sign-extended byte to fp32 (one v_cvt_f32_i32 with an SDWA byte select
+// each) and keep the upper halves of the results (exact: at most 8
+// significant bits, so the lower halves are zero).
 __device__ __forceinline__ void int8x4_to_bf16x4(uint32_t w, uint32_t& lo, uint32_t& hi) {
-  const uint32_t u = w ^ 0x80808080u;
-  // (float) of a byte extract selects v_cvt_f32_ubyte0..3
-  const float f0 = (float)(u & 0xffu) - 128.f;
-  const float f1 = (float)((u >> 8) & 0xffu) - 128.f;
-  const float f2 = (float)((u >> 16) & 0xffu) - 128.f;
-  const float f3 = (float)(u >> 24) - 128.f;
+  const float f0 = (float)(int8_t)(w & 0xffu);
+  const float f1 = (float)(int8_t)((w >> 8) & 0xffu);
+  const float f2 = (float)(int8_t)((w >> 16) & 0xffu);
+  const float f3 = (float)(int8_t)(w >> 24);
   // v_perm_b32: bytes 2,3 of the second operand, then bytes 2,3 of the first
   lo = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, f1), __builtin_bit_cast(uint32_t, f0), 0x07060302u);
   hi = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, f3), __builtin_bit_cast(uint32_t, f2), 0x07060302u);
