@@ -1144,12 +1144,13 @@ static hipError_t launch_partial_t(const DecodeArgs& a, dim3 grid, hipStream_t s
   return hipGetLastError();
 }
 
-// rv > 0: the VALU variant for up to rv rows (1, 2, 4 or 8); share = 2:
-// two waves per head, one 16-row block each (d = 256); else mb MFMA blocks.
+// rv > 0: the VALU variant for up to rv rows (1, 2, 4 or 8); share = 2, 4
+// or 8: that many waves per head split the rows, mb 16-row blocks each;
+// else mb MFMA blocks per wave, the waves of a head splitting the tiles.
 template <int D, int KVT, int MODE>
 static hipError_t launch_mb(const DecodeArgs& a, int mb, int rv, int share, dim3 grid, hipStream_t st,
                             hipEvent_t ev0, hipEvent_t ev1) {
-  // Row sharing: the combinations the planner picks (share_tiling in the
+  // Row sharing: the combinations the planner picks (plan_tiling in the
   // host code) and no others.
   constexpr int NLD = TileShape<D, KVT != kKvBf16>::NLD;
   if (share == 2) {
