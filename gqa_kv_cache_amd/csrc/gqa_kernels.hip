@@ -686,7 +686,8 @@ __global__ void __launch_bounds__(64 * partial_waves<SHARE>(), (partial_min_wave
   if constexpr (SHARED) {
     // Rows shared by the SHARE waves of a head: all walk every tile of the
     // chunk; wave `sub` loads and stages part `sub` of each tile into the
-    // head's LDS buffer of the tile's parity.  A step stages the next tile's
+    // head's LDS buffer of the tile's parity (waves past NLOADERS have no
+    // part and only compute).  A step stages the next tile's
     // part into the buffer the previous tile used, refills the staged
     // registers with the tile two beyond it, and computes the current tile;
     // the LDS-only barrier that ends the step makes the staged parts
