@@ -83,12 +83,55 @@ __device__ __forceinline__ uint2 quantize8(const uint4 x, float s, float y, bool
 }
 
 // Absolute maxima of this workgroup's T new tokens, per KV head, into smax
-// (fp32 bits; zeroed by the caller, then a barrier): one head at a time,
-// each thread keeping its own maximum over its items with U loads of K and
-// of V in flight, then a wave reduction and one LDS atomic per wave.
+// (fp32 bits; zeroed by the caller, then a barrier).
+//
+// When a token row's 8-element items (H_kv * d / 8 of them) divide the
+// workgroup's threads, the workgroup reads whole rows, contiguously: thread
+// t always meets item t % (items per row), so it always sees the same head
+// and keeps one maximum per tensor.  Lanes of one head then reduce with
+// cross-lane swaps (within the head's items, and across the rows a wave
+// covers), and one lane per head and wave does an LDS atomic.  Otherwise one
+// head at a time: each thread keeps its own maximum over its items, then a
+// wave reduction and one LDS atomic per wave.  U loads of K and of V are in
+// flight per thread either way.
 template <int U>
 __device__ __forceinline__ void block_absmax(const AppendArgs& a, int64_t in_base, int T, uint32_t* smax) {
   const int d8 = a.head_dim / 8;
+  const int rc = a.h_kv * d8;  // items per token row
+  if (kAppendThreads % rc == 0) {
+    const int total = T * rc;
+    float mk = 0.f, mv = 0.f;
+    for (int base = 0; base < total; base += U * kAppendThreads) {
+      uint4 kx[U], vx[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        int it = base + u * kAppendThreads + (int)threadIdx.x;
+        if (it >= total) it = it % rc;  // the same item of row 0: the same head, harmless for a maximum
+        kx[u] = *reinterpret_cast<const uint4*>(a.k_new + in_base + (int64_t)it * 8);
+        vx[u] = *reinterpret_cast<const uint4*>(a.v_new + in_base + (int64_t)it * 8);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        mk = fmaxf(mk, absmax8(kx[u]));
+        mv = fmaxf(mv, absmax8(vx[u]));
+      }
+    }
+    const int lane = threadIdx.x & 63;
+    for (int off = 1; off < d8; off <<= 1) {  // the head's items in a row
+      mk = fmaxf(mk, __shfl_xor(mk, off));
+      mv = fmaxf(mv, __shfl_xor(mv, off));
+    }
+    for (int off = rc; off < 64; off <<= 1) {  // the rows one wave covers
+      mk = fmaxf(mk, __shfl_xor(mk, off));
+      mv = fmaxf(mv, __shfl_xor(mv, off));
+    }
+    if (lane % d8 == 0 && lane < rc) {
+      const int g = ((int)threadIdx.x % rc) / d8;
+      atomicMax(&smax[2 * g], __builtin_bit_cast(uint32_t, mk));  // |x| >= 0: integer order = float order
+      atomicMax(&smax[2 * g + 1], __builtin_bit_cast(uint32_t, mv));
+    }
+    return;
+  }
   const int per_head = T * d8;
   for (int g = 0; g < a.h_kv; ++g) {
     float mk = 0.f, mv = 0.f;
