@@ -1,5 +1,5 @@
-"""CPU oracle for appending new K/V rows to a cache, with FP8 E4M3FN
-quantisation on write.
+"""CPU oracle for appending new K/V rows to a cache, with FP8 E4M3FN or
+int8 quantisation on write.
 
 TEST INFRASTRUCTURE ONLY.  Nothing on the product path imports, calls or
 links this module: only ``tests/``, ``__graft_entry__.smoke()`` and the
@@ -22,6 +22,12 @@ What the pages fix, and what is read into them:
   IEEE float32, as the kernel computes it, because it decides an integer
   code.  Ties go to the code with an even mantissa; a value that rounds to
   zero keeps its sign (code 0x80 for negative).
+* Int8 (a reading; the int8 KV-cache section of "Profiling down to the
+  register, then an extension that broke my assumptions twice" gives no
+  encoding): ``code = clamp(RNE_int(x / scale), -127, 127)``, the quotient
+  again in IEEE float32, ties to the even integer; ``first_block`` scales
+  are ``absmax / 127``.  The decode path reads any two's-complement code
+  (-128 included) as ``code * scale``; the append never writes -128.
 * Scale policies (a reading of a "streaming" scale): ``given`` -- the
   caller's scales are used as they are; ``first_block`` -- a request whose
   cache is empty before the append (n_b = 0) takes, per KV head, ``scale =
@@ -42,9 +48,10 @@ from __future__ import annotations
 
 import numpy as np
 
-from .reference import CONTIGUOUS, PAGED, FP8, BF16, e4m3fn_value, physical_row
+from .reference import CONTIGUOUS, PAGED, FP8, INT8, BF16, e4m3fn_value, physical_row
 
 E4M3FN_MAX = 448.0
+INT8_MAX = 127.0
 
 _POS = None  # (values, codes) of the 127 finite non-negative E4M3FN codes, ascending
 
@@ -90,10 +97,21 @@ def quantize(x_f32: np.ndarray, scale: float) -> np.ndarray:
     return e4m3fn_encode(y.astype(np.float64))
 
 
-def first_block_scale(x_f32: np.ndarray) -> np.float32:
-    """absmax / 448 in float32, or 1 when every value is zero."""
+def quantize_int8(x_f32: np.ndarray, scale: float) -> np.ndarray:
+    """Int8 codes (as uint8 bytes, two's complement) of float32 values x under
+    one scale: float32 quotient, round to the nearest integer with ties to
+    even, clamp to +-127."""
+    with np.errstate(over="ignore"):
+        y = np.asarray(x_f32, dtype=np.float32) / np.float32(scale)
+    r = np.clip(np.rint(y.astype(np.float64)), -INT8_MAX, INT8_MAX)
+    return r.astype(np.int64).astype(np.int8).view(np.uint8)
+
+
+def first_block_scale(x_f32: np.ndarray, qmax: float = E4M3FN_MAX) -> np.float32:
+    """absmax / qmax in float32 (448 for FP8, 127 for int8), or 1 when every
+    value is zero."""
     amax = np.float32(np.max(np.abs(np.asarray(x_f32, dtype=np.float32)))) if np.size(x_f32) else np.float32(0)
-    return np.float32(amax / np.float32(E4M3FN_MAX)) if amax > 0 else np.float32(1.0)
+    return np.float32(amax / np.float32(qmax)) if amax > 0 else np.float32(1.0)
 
 
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
@@ -114,6 +132,9 @@ def reference_append(*, k_cache, v_cache, k_new, v_new, seqlens, layout: str, kv
     ``physical_row(b, t, ...)`` of the cache viewed as [rows, H_kv, d]."""
     if layout not in (CONTIGUOUS, PAGED):
         raise ValueError("append writes contiguous or paged caches")
+    if kv_dtype not in (BF16, FP8, INT8):
+        raise ValueError(kv_dtype)
+    q8 = kv_dtype in (FP8, INT8)
     if policy not in ("given", "first_block"):
         raise ValueError(policy)
     k_new = np.asarray(k_new, dtype=np.uint16)
@@ -131,11 +152,11 @@ def reference_append(*, k_cache, v_cache, k_new, v_new, seqlens, layout: str, kv
         for g in range(Hkv):
             for new, rows, sc in ((k_new, rows_k, ks), (v_new, rows_v, vs)):
                 block = new[b, :, g, :]                      # [S, d] bf16 bits
-                if kv_dtype == FP8:
+                if q8:
                     x = bf16_bits_to_f32(block)
                     if policy == "first_block" and n == 0:
-                        sc[b, g] = first_block_scale(x)
-                    codes = quantize(x, float(sc[b, g]))
+                        sc[b, g] = first_block_scale(x, E4M3FN_MAX if kv_dtype == FP8 else INT8_MAX)
+                    codes = quantize(x, float(sc[b, g])) if kv_dtype == FP8 else quantize_int8(x, float(sc[b, g]))
                 for j in range(S):
                     t = n + j
                     if t < 0 or (layout == CONTIGUOUS and t >= capacity):
@@ -146,5 +167,5 @@ def reference_append(*, k_cache, v_cache, k_new, v_new, seqlens, layout: str, kv
                                      page_size=page_size)
                     if not 0 <= r < rows.shape[0]:
                         continue
-                    rows[r, g, :] = codes[j] if kv_dtype == FP8 else block[j]
+                    rows[r, g, :] = codes[j] if q8 else block[j]
     return kc, vc, ks, vs, (lens + S).astype(np.int32)

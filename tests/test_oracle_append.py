@@ -1,7 +1,8 @@
 """Pins for the append oracle (``oracle/append.py``): the E4M3FN encoder
 against the format's own values and torch's independent float8 cast, the
-first-block scale against its closed form, and the append against caches
-the input generator builds directly."""
+int8 quantiser against hand-worked ties and clamps and a half-step error
+bound, the first-block scales against their closed form, and the append
+against caches the input generator builds directly."""
 
 import numpy as np
 import pytest
@@ -61,6 +62,58 @@ def test_first_block_scale_closed_form():
     codes = A.quantize(x, float(s))
     assert codes[0, 1] == 0xFE                 # the absmax element lands on -448
     assert A.first_block_scale(np.zeros((3, 4), np.float32)) == np.float32(1.0)
+
+
+def test_int8_quantize_ties_to_even_and_clamps():
+    # x / s exactly halfway between integers goes to the even one; beyond
+    # +-127 clamps; a negative value that rounds to zero is code 0
+    x = np.array([2.5, 3.5, -2.5, -3.5, 0.5, -0.5, 1.5, 126.5, 127.5, 300.0, -300.0, -0.4, 0.0],
+                 dtype=np.float32)
+    want = [2, 4, -2, -4, 0, 0, 2, 126, 127, 127, -127, 0, 0]
+    assert A.quantize_int8(x, 1.0).view(np.int8).tolist() == want
+    # the same through a scale: 5 / 2 = 2.5 -> 2, 7 / 2 = 3.5 -> 4
+    assert A.quantize_int8(np.array([5.0, 7.0, -5.0], np.float32), 2.0).view(np.int8).tolist() == [2, 4, -2]
+
+
+def test_int8_round_trip_error_within_half_a_step():
+    # brute force over a range of bf16 values: |code * s - x| <= s / 2 inside
+    # the representable range, and codes are monotone in x
+    x = A.bf16_bits_to_f32(np.arange(1 << 16, dtype=np.uint32).astype(np.uint16))
+    x = np.sort(x[np.isfinite(x) & (np.abs(x) <= 2.0)])
+    s = np.float32(2.0 / 127)
+    codes = A.quantize_int8(x, float(s)).view(np.int8).astype(np.int64)
+    inside = np.abs(x.astype(np.float64)) <= 127 * float(s)
+    err = np.abs(codes * np.float64(s) - x.astype(np.float64))
+    assert np.all(err[inside] <= float(s) / 2 * (1 + 1e-6))
+    assert np.all(np.diff(codes) >= 0)
+    assert codes.min() == -127 and codes.max() == 127
+
+
+def test_int8_first_block_scale_closed_form():
+    x = np.array([[0.5, -3.0, 2.0], [1.0, 0.0, -0.25]], dtype=np.float32)
+    s = A.first_block_scale(x, A.INT8_MAX)
+    assert s == np.float32(3.0) / np.float32(127.0)
+    codes = A.quantize_int8(x, float(s)).view(np.int8)
+    assert codes[0, 1] == -127                 # the absmax element lands on -127
+    assert A.first_block_scale(np.zeros((3, 4), np.float32), A.INT8_MAX) == np.float32(1.0)
+
+
+def test_int8_append_is_read_back_by_the_decode_oracle_within_half_a_step():
+    rng = np.random.default_rng(4)
+    B, S, Hkv, d, cap = 2, 5, 3, 64, 8
+    x = rng.standard_normal((B, S, Hkv, d)).astype(np.float32)
+    k_new = gi.f32_to_bf16_bits(x)
+    v_new = gi.f32_to_bf16_bits(-x)
+    kc = np.zeros((B, cap, Hkv, d), np.uint8)
+    kc2, vc2, ks, vs, lens = A.reference_append(k_cache=kc, v_cache=kc.copy(), k_new=k_new, v_new=v_new,
+                                                seqlens=np.zeros(B, np.int32), layout=R.CONTIGUOUS,
+                                                kv_dtype=R.INT8, capacity=cap, k_scale=np.zeros((B, Hkv), np.float32),
+                                                v_scale=np.zeros((B, Hkv), np.float32), policy="first_block")
+    assert lens.tolist() == [S, S]
+    xb = A.bf16_bits_to_f32(k_new).astype(np.float64)
+    back = R.int8_codes_to_f64(kc2[:, :S]) * ks[:, None, :, None]
+    assert np.all(np.abs(back - xb) <= ks[:, None, :, None] / 2 * (1 + 1e-6))
+    assert np.array_equal(kc2[:, S:], np.zeros_like(kc2[:, S:]))    # rows past the append untouched
 
 
 def _split(w: gi.Workload, n_keep):
@@ -203,7 +256,9 @@ _PINS = [test_every_finite_code_round_trips, test_midpoints_go_to_even_mantissa,
          lambda: test_append_rebuilds_generated_bf16_cache(gi.LAYOUT_CONTIGUOUS),
          lambda: test_append_rebuilds_generated_bf16_cache(gi.LAYOUT_PAGED),
          test_first_block_append_matches_generator_quantiser, test_later_appends_keep_the_scale_and_clamp,
-         test_append_writes_only_target_rows_paged, test_positions_without_a_row_are_not_written]
+         test_append_writes_only_target_rows_paged, test_positions_without_a_row_are_not_written,
+         test_int8_quantize_ties_to_even_and_clamps, test_int8_round_trip_error_within_half_a_step,
+         test_int8_first_block_scale_closed_form, test_int8_append_is_read_back_by_the_decode_oracle_within_half_a_step]
 
 _orig_encode = A.e4m3fn_encode
 _orig_quantize = A.quantize
@@ -238,14 +293,25 @@ def _multiply_scale(x, scale):
     return _orig_encode(y.astype(np.float64))
 
 
-def _scale_over_max_code(x):
+def _scale_over_max_code(x, qmax=A.E4M3FN_MAX):
     amax = np.float32(np.max(np.abs(np.asarray(x, np.float32))))
     return np.float32(amax / np.float32(240.0)) if amax > 0 else np.float32(1.0)
 
 
-def _zero_scale_kept(x):
+def _zero_scale_kept(x, qmax=A.E4M3FN_MAX):
     amax = np.float32(np.max(np.abs(np.asarray(x, np.float32))))
-    return np.float32(amax / np.float32(448.0)) if amax > 0 else np.float32(0.0)
+    return np.float32(amax / np.float32(qmax)) if amax > 0 else np.float32(0.0)
+
+
+def _int8_ties_away(x, scale):
+    y = (np.asarray(x, np.float32) / np.float32(scale)).astype(np.float64)
+    r = np.clip(np.sign(y) * np.floor(np.abs(y) + 0.5), -127, 127)
+    return r.astype(np.int64).astype(np.int8).view(np.uint8)
+
+
+def _int8_clamp_128(x, scale):
+    y = (np.asarray(x, np.float32) / np.float32(scale)).astype(np.float64)
+    return np.clip(np.rint(y), -128, 127).astype(np.int64).astype(np.int8).view(np.uint8)
 
 
 def _one_past(b, t, layout, **kw):
@@ -260,6 +326,8 @@ MUTATIONS = {
     "scale over the wrong maximum": ("first_block_scale", _scale_over_max_code),
     "zero block gets scale 0": ("first_block_scale", _zero_scale_kept),
     "written one token late": ("physical_row", _one_past),
+    "int8 ties away from zero": ("quantize_int8", _int8_ties_away),
+    "int8 clamps to -128": ("quantize_int8", _int8_clamp_128),
 }
 
 
