@@ -380,7 +380,8 @@ gqa_status check_append(const gqa_append_params* p) {
     return fail(GQA_ERR_UNSUPPORTED, "h_kv must be 1..%d", gqa::kAppendMaxHeads);
   if (p->head_dim != 64 && p->head_dim != 128 && p->head_dim != 256)
     return fail(GQA_ERR_UNSUPPORTED, "head_dim %d not built (64, 128, 256)", p->head_dim);
-  if (p->kv_dtype != GQA_KV_BF16 && p->kv_dtype != GQA_KV_FP8_E4M3FN) return fail(GQA_ERR_INVALID_ARG, "bad kv_dtype");
+  if (p->kv_dtype != GQA_KV_BF16 && p->kv_dtype != GQA_KV_FP8_E4M3FN && p->kv_dtype != GQA_KV_INT8)
+    return fail(GQA_ERR_INVALID_ARG, "bad kv_dtype");
   if (p->scale_policy != GQA_SCALE_GIVEN && p->scale_policy != GQA_SCALE_FIRST_BLOCK)
     return fail(GQA_ERR_INVALID_ARG, "bad scale_policy");
   if (p->kv_rows < 1) return fail(GQA_ERR_INVALID_ARG, "kv_rows must be >= 1");
@@ -409,7 +410,7 @@ int append_chunk_tokens(const gqa_append_params* p) {
 
 size_t append_workspace(const gqa_append_params* p) {
   const int chunks = (int)cdiv(p->s_new, append_chunk_tokens(p));
-  if (p->kv_dtype != GQA_KV_FP8_E4M3FN || p->scale_policy != GQA_SCALE_FIRST_BLOCK || chunks == 1) return 0;
+  if (p->kv_dtype == GQA_KV_BF16 || p->scale_policy != GQA_SCALE_FIRST_BLOCK || chunks == 1) return 0;
   return (size_t)p->batch * chunks * 2 * p->h_kv * sizeof(uint32_t);
 }
 
@@ -571,8 +572,8 @@ gqa_status gqa_kv_append(const gqa_append_params* p, const void* k_new, const vo
   if (seqlens_out && seqlens_out == seqlens)
     return fail(GQA_ERR_INVALID_ARG, "seqlens_out must not alias seqlens");
   if (p->layout == GQA_LAYOUT_PAGED && !block_table) return fail(GQA_ERR_INVALID_ARG, "paged layout needs block_table");
-  const bool fp8 = p->kv_dtype == GQA_KV_FP8_E4M3FN;
-  if (fp8 && (!k_scale || !v_scale)) return fail(GQA_ERR_INVALID_ARG, "FP8 caches need k_scale and v_scale");
+  const bool fp8 = p->kv_dtype != GQA_KV_BF16;  // one-byte codes with scales
+  if (fp8 && (!k_scale || !v_scale)) return fail(GQA_ERR_INVALID_ARG, "FP8 and int8 caches need k_scale and v_scale");
   if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16))
     return fail(GQA_ERR_ALIGNMENT, "k_new, v_new, k_cache and v_cache must be 16-byte aligned");
   const void* small[] = {seqlens, seqlens_out, block_table, k_scale, v_scale};
@@ -605,6 +606,7 @@ gqa_status gqa_kv_append(const gqa_append_params* p, const void* k_new, const vo
   a.head_dim = p->head_dim;
   a.paged = p->layout == GQA_LAYOUT_PAGED;
   a.fp8 = fp8;
+  a.int8 = p->kv_dtype == GQA_KV_INT8;
   a.first_block = p->scale_policy == GQA_SCALE_FIRST_BLOCK;
   a.seq_cap = p->seq_capacity;
   a.page_shift = a.paged ? log2_exact(p->page_size) : 0;

@@ -1,11 +1,12 @@
-// K/V append with FP8 E4M3FN quantisation on write (gfx950).
+// K/V append with FP8 E4M3FN or int8 quantisation on write (gfx950).
 //
 // Writes the S_new bf16 K and V rows of each request at logical positions
 // n_b .. n_b + S_new - 1 of a contiguous or paged cache, as bf16 or as FP8
-// E4M3FN codes under one scale per (request, KV head) -- the storage the
-// decode kernels read ("Sparse paged GQA decode attention with FP8 KV cache
-// on SM89", "Workload" and "Implementations").  Only the appended rows are
-// touched.
+// E4M3FN or int8 codes under one scale per (request, KV head) -- the
+// storage the decode kernels read ("Sparse paged GQA decode attention with
+// FP8 KV cache on SM89", "Workload" and "Implementations"; the int8
+// KV-cache section of "Profiling down to the register, then an extension
+// that broke my assumptions twice").  Only the appended rows are touched.
 //
 // Work split: a workgroup takes `chunk_tokens` consecutive new tokens of one
 // request, all KV heads (a token's H_kv * d elements are contiguous in both
@@ -18,8 +19,8 @@
 // corrected reciprocal and the hardware convert at 4.8 TB/s, against 5.2
 // TB/s for a plain device-to-device copy of the same bytes.
 //
-// First-block scales: a request with n_b == 0 takes scale = absmax / 448 per
-// KV head over its appended rows.  One workgroup per request reduces its
+// First-block scales: a request with n_b == 0 takes scale = absmax / 448
+// (FP8) or absmax / 127 (int8) per KV head over its appended rows.  One workgroup per request reduces its
 // rows in LDS; when a request's rows span several workgroups, a first pass
 // writes each workgroup's per-head maxima to the workspace and a
 // per-request pass reduces them to the scales (no atomics in HBM, no
@@ -80,6 +81,23 @@ __device__ __forceinline__ uint2 quantize8(const uint4 x, float s, float y, bool
   int hi = __builtin_amdgcn_cvt_pk_fp8_f32(q[4], q[5], 0, false);
   hi = __builtin_amdgcn_cvt_pk_fp8_f32(q[6], q[7], hi, true);
   return uint2{(uint32_t)lo, (uint32_t)hi};
+}
+
+// Int8 codes of eight bf16 values: the same fp32 quotient, rounded to the
+// nearest integer with ties to even (v_rndne_f32), clamped to +-127, packed
+// as two's-complement bytes (lowest element in the lowest byte).  Clamping
+// before rounding gives the same code: +-127 are integers.
+__device__ __forceinline__ uint2 quantize_i8(const uint4 x, float s, float y, bool exact) {
+  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+  uint32_t b[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float q0 = fminf(fmaxf(quotient(bf16_to_f32(w[i] & 0xffffu), s, y, exact), -127.f), 127.f);
+    const float q1 = fminf(fmaxf(quotient(bf16_to_f32(w[i] >> 16), s, y, exact), -127.f), 127.f);
+    b[2 * i] = (uint32_t)(int)__builtin_rintf(q0) & 0xffu;
+    b[2 * i + 1] = (uint32_t)(int)__builtin_rintf(q1) & 0xffu;
+  }
+  return uint2{b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24), b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24)};
 }
 
 // Absolute maxima of this workgroup's T new tokens, per KV head, into smax
@@ -203,6 +221,7 @@ __global__ void __launch_bounds__(kAppendThreads) gqa_append_kernel(AppendArgs a
   if (PASS != 1 && !calib) return;
   const int d8 = a.head_dim / 8;
   const int per_tok = a.h_kv * d8;  // 8-element items per token row
+  const float qmax = a.int8 ? 127.f : 448.f;  // largest code magnitude
 
   if (PASS == 2) {
     // per-request reduction of the per-workgroup maxima
@@ -214,7 +233,7 @@ __global__ void __launch_bounds__(kAppendThreads) gqa_append_kernel(AppendArgs a
     __syncthreads();
     for (int i = threadIdx.x; i < 2 * a.h_kv; i += kAppendThreads) {
       const float amax = __builtin_bit_cast(float, smax[i]);
-      ((i & 1) ? a.v_scale : a.k_scale)[(int64_t)b * a.h_kv + (i >> 1)] = amax > 0.f ? amax / 448.f : 1.f;
+      ((i & 1) ? a.v_scale : a.k_scale)[(int64_t)b * a.h_kv + (i >> 1)] = amax > 0.f ? amax / qmax : 1.f;
     }
     return;
   }
@@ -236,7 +255,7 @@ __global__ void __launch_bounds__(kAppendThreads) gqa_append_kernel(AppendArgs a
     }
     for (int i = threadIdx.x; i < 2 * a.h_kv; i += kAppendThreads) {
       const float amax = __builtin_bit_cast(float, smax[i]);
-      const float s = amax > 0.f ? amax / 448.f : 1.f;
+      const float s = amax > 0.f ? amax / qmax : 1.f;
       sscale[i] = s;
       ((i & 1) ? a.v_scale : a.k_scale)[(int64_t)b * a.h_kv + (i >> 1)] = s;
     }
@@ -275,8 +294,13 @@ __global__ void __launch_bounds__(kAppendThreads) gqa_append_kernel(AppendArgs a
         const int g = r / d8;
         const float sk = sscale[2 * g], sv = sscale[2 * g + 1];
         const float yk = sinv[2 * g], yv = sinv[2 * g + 1];
-        *reinterpret_cast<uint2*>(a.k_cache + dst) = quantize8(kx[u], sk, yk, !(yk < INFINITY));
-        *reinterpret_cast<uint2*>(a.v_cache + dst) = quantize8(vx[u], sv, yv, !(yv < INFINITY));
+        if (a.int8) {
+          *reinterpret_cast<uint2*>(a.k_cache + dst) = quantize_i8(kx[u], sk, yk, !(yk < INFINITY));
+          *reinterpret_cast<uint2*>(a.v_cache + dst) = quantize_i8(vx[u], sv, yv, !(yv < INFINITY));
+        } else {
+          *reinterpret_cast<uint2*>(a.k_cache + dst) = quantize8(kx[u], sk, yk, !(yk < INFINITY));
+          *reinterpret_cast<uint2*>(a.v_cache + dst) = quantize8(vx[u], sv, yv, !(yv < INFINITY));
+        }
       } else {
         *reinterpret_cast<uint4*>(a.k_cache + dst) = kx[u];
         *reinterpret_cast<uint4*>(a.v_cache + dst) = vx[u];

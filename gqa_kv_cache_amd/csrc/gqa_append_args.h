@@ -20,14 +20,15 @@ struct AppendArgs {
   const int32_t* seqlens;  // [B] n_b before the call
   int32_t* seqlens_out;    // [B] or null
   const int32_t* block_table;
-  uint8_t* k_cache;  // token rows [kv_rows, H_kv, d] of 1 (FP8) or 2 (bf16) bytes
+  uint8_t* k_cache;  // token rows [kv_rows, H_kv, d] of 1 (FP8, int8) or 2 (bf16) bytes
   uint8_t* v_cache;
   float* k_scale;  // [B, H_kv]
   float* v_scale;
   uint32_t* amax;  // workspace [B, chunks, H_kv, 2]: fp32 bits of per-workgroup maxima
   int64_t kv_rows;
   int32_t batch, s_new, h_kv, head_dim;
-  int32_t paged, fp8, first_block;
+  int32_t paged, fp8, first_block;  // fp8: one-byte codes with scales (FP8 E4M3FN, or int8 when int8)
+  int32_t int8;
   int32_t seq_cap, page_shift, max_pages;
   int32_t chunk_tokens, chunks;
 };

@@ -1,9 +1,9 @@
-"""K/V append with FP8 quantise-on-write, through the C ABI, against the
-append oracle: every byte of both caches, the scales and the new lengths
+"""K/V append with FP8 or int8 quantise-on-write, through the C ABI, against
+the append oracle: every byte of both caches, the scales and the new lengths
 bit for bit (needs a gfx950 GPU).  Cases cover contiguous and paged caches,
-bf16 and FP8, both scale policies, single- and multi-workgroup requests,
-positions past the capacity, every finite bf16 value through the encoder,
-and an append followed by a decode."""
+bf16, FP8 and int8, both scale policies, single- and multi-workgroup
+requests, positions past the capacity, every finite bf16 value through the
+encoders, and an append followed by a decode."""
 
 import numpy as np
 import pytest
@@ -40,7 +40,7 @@ def new_rows(rng, B, S, Hkv, d, spread=True):
 def run_case(*, layout, kv_dtype, policy, B, S, Hkv, d, lens, cap=0, P=16, pages_per_seq=0, scales=None,
              seed=0, k_new=None, v_new=None):
     rng = np.random.default_rng(seed)
-    fp8 = kv_dtype == R.FP8
+    fp8 = kv_dtype in (R.FP8, R.INT8)    # one-byte codes with scales
     esz = np.uint8 if fp8 else np.uint16
     if layout == R.CONTIGUOUS:
         shape = (B, cap, Hkv, d)
@@ -50,10 +50,10 @@ def run_case(*, layout, kv_dtype, policy, B, S, Hkv, d, lens, cap=0, P=16, pages
         shape = (pool, P, Hkv, d)
         bt = rng.permutation(pool)[: B * pages_per_seq].reshape(B, pages_per_seq).astype(np.int32)
     kc = rng.integers(0, 256 if fp8 else 1 << 16, size=shape).astype(esz)
-    if fp8:
+    if kv_dtype == R.FP8:
         kc[(kc & 0x7F) == 0x7F] = 0      # keep the sentinel bytes finite codes
     vc = rng.integers(0, 256 if fp8 else 1 << 16, size=shape).astype(esz)
-    if fp8:
+    if kv_dtype == R.FP8:
         vc[(vc & 0x7F) == 0x7F] = 0
     k_new = new_rows(rng, B, S, Hkv, d) if k_new is None else k_new
     v_new = new_rows(rng, B, S, Hkv, d) if v_new is None else v_new
@@ -93,7 +93,7 @@ def run_case(*, layout, kv_dtype, policy, B, S, Hkv, d, lens, cap=0, P=16, pages
 
 
 @pytest.mark.parametrize("layout", [R.CONTIGUOUS, R.PAGED])
-@pytest.mark.parametrize("kv_dtype", [R.BF16, R.FP8])
+@pytest.mark.parametrize("kv_dtype", [R.BF16, R.FP8, R.INT8])
 @pytest.mark.parametrize("S", [1, 3, 40])
 def test_append_given_scales(layout, kv_dtype, S):
     B, Hkv, d = 5, 4, 128
@@ -102,21 +102,23 @@ def test_append_given_scales(layout, kv_dtype, S):
              pages_per_seq=10, seed=S)
 
 
+@pytest.mark.parametrize("kv_dtype", [R.FP8, R.INT8])
 @pytest.mark.parametrize("layout", [R.CONTIGUOUS, R.PAGED])
 @pytest.mark.parametrize("S", [1, 8, 33, 700])
-def test_append_first_block(layout, S):
+def test_append_first_block(layout, S, kv_dtype):
     # 700 new tokens of 8 heads x d 128 span several workgroups per request:
     # the per-workgroup maxima go through the workspace
     B, Hkv, d = 4, 8, 128
     lens = [0, 5, 0, 64]
-    run_case(layout=layout, kv_dtype=R.FP8, policy="first_block", B=B, S=S, Hkv=Hkv, d=d, lens=lens, cap=800,
+    run_case(layout=layout, kv_dtype=kv_dtype, policy="first_block", B=B, S=S, Hkv=Hkv, d=d, lens=lens, cap=800,
              pages_per_seq=52, seed=100 + S)
 
 
+@pytest.mark.parametrize("kv_dtype", [R.FP8, R.INT8])
 @pytest.mark.parametrize("d,Hkv", [(64, 1), (64, 3), (256, 2), (256, 8)])
-def test_append_head_shapes(d, Hkv):
+def test_append_head_shapes(d, Hkv, kv_dtype):
     for policy in ("given", "first_block"):
-        run_case(layout=R.PAGED, kv_dtype=R.FP8, policy=policy, B=3, S=21, Hkv=Hkv, d=d, lens=[0, 3, 40],
+        run_case(layout=R.PAGED, kv_dtype=kv_dtype, policy=policy, B=3, S=21, Hkv=Hkv, d=d, lens=[0, 3, 40],
                  pages_per_seq=5, P=16, seed=d + Hkv)
 
 
@@ -149,17 +151,19 @@ def _every_bf16_row():
     return bits
 
 
+@pytest.mark.parametrize("kv_dtype", [R.FP8, R.INT8])
 @pytest.mark.parametrize("scale", [1.0, 0.125, 0.0137, 3.0])
-def test_encoder_on_every_bf16_value(scale):
+def test_encoder_on_every_bf16_value(scale, kv_dtype):
     # one token row of 256 heads x d 256 = 65536 elements: every bf16 bit
     # pattern once, under one scale
     k_new = _every_bf16_row().reshape(1, 1, 256, 256)
     v_new = k_new[:, :, ::-1, ::-1].copy()
-    run_case(layout=R.CONTIGUOUS, kv_dtype=R.FP8, policy="given", B=1, S=1, Hkv=256, d=256, lens=[0], cap=2,
+    run_case(layout=R.CONTIGUOUS, kv_dtype=kv_dtype, policy="given", B=1, S=1, Hkv=256, d=256, lens=[0], cap=2,
              scales=np.full((1, 256), scale, np.float32), k_new=k_new, v_new=v_new)
 
 
-def test_encoder_on_every_bf16_value_under_many_scales():
+@pytest.mark.parametrize("kv_dtype", [R.FP8, R.INT8])
+def test_encoder_on_every_bf16_value_under_many_scales(kv_dtype):
     # 32 requests x 256 heads of per-head scales -- log-uniform over 2^-40 ..
     # 2^40, powers of two (exact quotients, many exact ties), and the ends:
     # a subnormal scale whose reciprocal overflows, a subnormal one whose
@@ -173,14 +177,15 @@ def test_encoder_on_every_bf16_value_under_many_scales():
     row = _every_bf16_row()
     k_new = np.stack([np.roll(row, 997 * b) for b in range(B)]).reshape(B, 1, H, d)
     v_new = k_new[:, :, ::-1, ::-1].copy()
-    run_case(layout=R.CONTIGUOUS, kv_dtype=R.FP8, policy="given", B=B, S=1, Hkv=H, d=d, lens=[0] * B, cap=1,
+    run_case(layout=R.CONTIGUOUS, kv_dtype=kv_dtype, policy="given", B=B, S=1, Hkv=H, d=d, lens=[0] * B, cap=1,
              scales=scales, k_new=k_new, v_new=v_new)
 
 
-def test_append_then_decode():
-    # A decode step: the new token's K/V are appended (FP8, first-block
-    # scales for the empty request), then attention runs over the cache --
-    # against the oracle's decode of the oracle's appended cache.
+@pytest.mark.parametrize("kv_dtype", [R.FP8, R.INT8])
+def test_append_then_decode(kv_dtype):
+    # A decode step: the new token's K/V are appended (first-block scales
+    # for the empty request), then attention runs over the cache -- against
+    # the oracle's decode of the oracle's appended cache.
     rng = np.random.default_rng(9)
     B, Hq, Hkv, d, P, pps = 3, 16, 4, 128, 16, 8
     lens = np.array([0, 37, 100], np.int32)
@@ -196,17 +201,18 @@ def test_append_then_decode():
     for b in range(B):
         for t in range(int(lens[b])):
             r = bt[b, t // P] * P + t % P
-            kc.reshape(-1, Hkv, d)[r] = A.quantize(rng.standard_normal((Hkv, d)).astype(np.float32) * 0.5, 0.01)
-            vc.reshape(-1, Hkv, d)[r] = A.quantize(rng.standard_normal((Hkv, d)).astype(np.float32) * 0.5, 0.01)
+            qz = A.quantize if kv_dtype == R.FP8 else A.quantize_int8
+            kc.reshape(-1, Hkv, d)[r] = qz(rng.standard_normal((Hkv, d)).astype(np.float32) * 0.5, 0.01)
+            vc.reshape(-1, Hkv, d)[r] = qz(rng.standard_normal((Hkv, d)).astype(np.float32) * 0.5, 0.01)
     k_new = new_rows(rng, B, S, Hkv, d, spread=False)
     v_new = new_rows(rng, B, S, Hkv, d, spread=False)
-    kc2, vc2, ks2, vs2, lens2 = run_case(layout=R.PAGED, kv_dtype=R.FP8, policy="first_block", B=B, S=S, Hkv=Hkv,
+    kc2, vc2, ks2, vs2, lens2 = run_case(layout=R.PAGED, kv_dtype=kv_dtype, policy="first_block", B=B, S=S, Hkv=Hkv,
                                          d=d, lens=lens, P=P, pages_per_seq=pps, scales=ks, k_new=k_new, v_new=v_new)
     # decode over the appended cache (the oracle's bytes, which the GPU
     # matched exactly above)
     q = gi.f32_to_bf16_bits(rng.standard_normal((B, S, Hq, d)).astype(np.float32))
     spec = gi.Spec(name="append-decode", batch=B, h_q=Hq, h_kv=Hkv, head_dim=d, s_q=S, causal=True,
-                   layout=gi.LAYOUT_PAGED, page_size=P, kv_dtype=gi.KV_FP8, fixed_lengths=tuple(int(x) for x in lens2))
+                   layout=gi.LAYOUT_PAGED, page_size=P, kv_dtype=kv_dtype, fixed_lengths=tuple(int(x) for x in lens2))
     w = gi.Workload(spec=spec, seed=0, q=q, k_cache=kc2, v_cache=vc2, seqlens=lens2, cu_seqlens=None,
                     block_table=bt, topk_idx=None, k_scale=ks2, v_scale=vs2, gate=None)
     up = Uploaded(w)
