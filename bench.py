@@ -164,6 +164,8 @@ def main():
     ap.add_argument("--scale-policy", default=None, choices=["given", "first_block"],
                     help="append: scale policy (default: the workload's)")
     ap.add_argument("--kv-chunk", type=int, default=0, help="force list positions per workgroup")
+    ap.add_argument("--append-dtype", default="fp8_e4m3fn", choices=["fp8_e4m3fn", "int8"],
+                    help="--op append: the code type written to the cache")
     ap.add_argument("--math", default="auto", choices=["auto", "mfma", "valu"],
                     help="math path of the partial kernel (auto: the planner's measured choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -394,7 +396,7 @@ def calibrate_copy(torch, stream) -> float:
     return round(2 * (512 << 20) / t_copy / 1e9, 1)
 
 
-APPEND_METRIC = "GB/s over the bytes moved, K/V append with FP8 quantise-on-write (paged pool)"
+APPEND_METRIC = "GB/s over the bytes moved, K/V append with quantise-on-write (paged pool)"
 
 
 def bench_append(args):
@@ -424,7 +426,8 @@ def bench_append(args):
     bt = torch.from_numpy(w.block_table).to(dev)
     ks = torch.from_numpy(w.k_scale).to(dev)
     vs = torch.from_numpy(w.v_scale).to(dev)
-    p = G.make_append_params(batch=B, s_new=S, h_kv=Hkv, head_dim=d, layout="paged", kv_dtype="fp8_e4m3fn",
+    kvd = args.append_dtype
+    p = G.make_append_params(batch=B, s_new=S, h_kv=Hkv, head_dim=d, layout="paged", kv_dtype=kvd,
                              scale_policy=policy, kv_rows=w.pool_pages * P, page_size=P, max_pages_per_seq=pps)
     wsb = G.gqa_kv_append_workspace_size(p)
     ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
@@ -477,9 +480,9 @@ def bench_append(args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16->fp8_e4m3fn",
+        "dtype": f"bf16->{kvd}",
         "data": "synthetic",
-        "config": {"workload": name, "batch": B, "new_tokens": S, "h_kv": Hkv, "head_dim": d,
+        "config": {"workload": name, "batch": B, "new_tokens": S, "h_kv": Hkv, "head_dim": d, "kv_dtype": kvd,
                    "stored_tokens": int(w.seqlens[0]), "layout": "paged", "page_size": P,
                    "scale_policy": policy, "seed": w.seed, "passes": 2 if two_pass else 1},
         "us_per_call": round(us_per_call, 3),
@@ -501,7 +504,7 @@ def bench_append(args):
     ok = True
     if not args.no_cpu_baseline:
         say("timing the CPU append oracle on a bounded sample and checking sampled requests")
-        res, chk = append_baseline_and_check(w, policy, kc, vc, ks, vs, so)
+        res, chk = append_baseline_and_check(w, policy, kc, vc, ks, vs, so, kv_dtype=kvd)
         line["cpu_baseline"] = res
         line["check"] = chk
         ok = chk["ok"]
@@ -511,7 +514,7 @@ def bench_append(args):
         sys.exit(1)
 
 
-def append_baseline_and_check(w, policy, kc, vc, ks, vs, so, budget_s: float = 10.0):
+def append_baseline_and_check(w, policy, kc, vc, ks, vs, so, kv_dtype="fp8_e4m3fn", budget_s: float = 10.0):
     """Run the append oracle request by request (each on a compact pool of
     its own pages) until about budget_s of CPU time; time it, and compare
     every byte of those requests' pages and their scales with the GPU's."""
@@ -530,7 +533,7 @@ def append_baseline_and_check(w, policy, kc, vc, ks, vs, so, budget_s: float = 1
         t = time.perf_counter()
         ok_k, ok_v, rks, rvs, lens = A.reference_append(
             k_cache=zero, v_cache=zero, k_new=w.k_new[b:b + 1], v_new=w.v_new[b:b + 1],
-            seqlens=w.seqlens[b:b + 1], layout="paged", kv_dtype="fp8_e4m3fn", block_table=bt, page_size=P,
+            seqlens=w.seqlens[b:b + 1], layout="paged", kv_dtype=kv_dtype, block_table=bt, page_size=P,
             k_scale=w.k_scale[b:b + 1], v_scale=w.v_scale[b:b + 1], policy=policy)
         t_oracle += time.perf_counter() - t
         n0 = int(w.seqlens[b])
