@@ -43,9 +43,14 @@ duplicates count once per occurrence; the gate is elementwise with O's shape
 (a headwise gate broadcasts over d); the paged pool is laid out
 [pages, page_size, H_kv, d].
 
-Parity pins for every function here live in ``tests/test_oracle_*.py``.
-The gate-shape convention is a reading, not a pinned fact ("parity
-unpinned" for the gate's shape; its arithmetic is pinned by closed forms).
+Parity pins for every function here live in ``tests/test_oracle_*.py``:
+every branch -- each layout, top-K masking, causal blocks, FP8 and int8
+codes, a given (also negative) softmax scale, the elementwise and the
+headwise gate -- is checked against an independently written brute force
+on tiny inputs, and planted bugs in each of them fail at least one pin.
+Which gate shape the pages mean is still a reading (they name a gate
+tensor beside the query and output, and a sigmoid after attention); both
+shapes are built and pinned.
 """
 
 from __future__ import annotations
@@ -203,6 +208,26 @@ def sigmoid(x: np.ndarray) -> np.ndarray:
     return 1.0 / (1.0 + np.exp(-x))
 
 
+def score_scale(head_dim: int, softmax_scale: Optional[float] = None) -> float:
+    """Multiplier of q.k: the caller's scale when one is given (None or 0
+    means none), else 1/sqrt(d) -- the tiny workload's definition.  Any
+    other value, negative ones included, is used as given: the pages fold
+    one multiplier into the scores ("Sparse paged GQA decode attention with
+    FP8 KV cache on SM89", section "Implementations") and nothing there
+    restricts its sign."""
+    return (1.0 / math.sqrt(head_dim)) if not softmax_scale else float(softmax_scale)
+
+
+def gate_factor(gate, gate_mode: str, b: int, i: int, h: int):
+    """sigmoid(gate) for the output row of request b, query i, head h: the
+    d values gate[b, i, h, :] (elementwise gate, O's shape) or the one value
+    gate[b, i, h] (headwise gate [B, S_q, H_q], the same for every column).
+    Same page, section "Workload": a sigmoid gate applied after attention."""
+    if gate_mode == "headwise":
+        return sigmoid(bf16_bits_to_f64(gate[b, i, h]))
+    return sigmoid(bf16_bits_to_f64(gate[b, i, h, :]))
+
+
 def reference_decode(*, q, k_cache, v_cache, h_q: int, h_kv: int, head_dim: int,
                      s_q: int, layout: str, seqlens=None, cu_seqlens=None,
                      block_table=None, page_size: int = 16, topk_idx=None,
@@ -220,7 +245,7 @@ def reference_decode(*, q, k_cache, v_cache, h_q: int, h_kv: int, head_dim: int,
     d = head_dim
     assert q.shape == (B, s_q, h_q, d)
     assert h_q % h_kv == 0
-    scale = (1.0 / math.sqrt(d)) if not softmax_scale else float(softmax_scale)
+    scale = score_scale(d, softmax_scale)
     fp8 = kv_dtype == FP8
     int8 = kv_dtype == INT8
     capacity = k_cache.shape[1] if layout == CONTIGUOUS else 0
@@ -252,11 +277,7 @@ def reference_decode(*, q, k_cache, v_cache, h_q: int, h_kv: int, head_dim: int,
         qv = bf16_bits_to_f64(q[b, i, h, :])
         out, lse = softmax_attend(qv, Kh, Vh, scale)
         if gate is not None:
-            if gate_mode == "headwise":
-                gv = bf16_bits_to_f64(gate[b, i, h])
-            else:
-                gv = bf16_bits_to_f64(gate[b, i, h, :])
-            out = out * sigmoid(gv)
+            out = out * gate_factor(gate, gate_mode, b, i, h)
         O[b, i, h, :] = out
         LSE[b, h, i] = lse
     return O, LSE

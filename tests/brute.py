@@ -10,7 +10,8 @@ Differences from the oracle, on purpose:
   * the KV head of a query head comes from splitting the H_q heads into
     H_kv equal consecutive groups;
   * softmax is evaluated without max subtraction, LSE directly as
-    log(sum exp), using ``math.fsum`` over Python floats.
+    log(sum exp), using ``math.fsum`` over Python floats;
+  * a headwise gate is widened to the elementwise shape before use.
 """
 
 from __future__ import annotations
@@ -67,17 +68,27 @@ def _inverse_rows(w):
     return out
 
 
-def brute_decode(w, softmax_scale=None):
+def brute_decode(w, softmax_scale=None, headwise_gate=None):
+    """fp64 outputs (O [B, S_q, H_q, d], LSE [B, H_q, S_q]) of workload w.
+
+    softmax_scale: the score multiplier (None: 1/sqrt(d)).  headwise_gate:
+    bf16 bits [B, S_q, H_q] used instead of w.gate, one value per head; it
+    is widened here to an elementwise gate by repeating each head's value
+    over the d columns, so both gate shapes go through the same loop."""
     s = w.spec
     B, Sq, Hq, Hkv, d = s.batch, s.s_q, s.h_q, s.h_kv, s.head_dim
-    scale = softmax_scale if softmax_scale else 1.0 / math.sqrt(d)
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     groups = np.array_split(np.arange(Hq), Hkv)
     head_of = {int(h): gi for gi, grp in enumerate(groups) for h in grp}
     dec = {"fp8_e4m3fn": _decode_fp8, "int8": _decode_int8}.get(s.kv_dtype, _decode_bf16)
     K = dec(w.k_cache).reshape(-1, Hkv, d)
     V = dec(w.v_cache).reshape(-1, Hkv, d)
     q = _decode_bf16(w.q)
-    gate = _decode_bf16(w.gate) if w.gate is not None else None
+    if headwise_gate is not None:
+        assert headwise_gate.shape == (B, Sq, Hq)
+        gate = np.repeat(_decode_bf16(headwise_gate)[:, :, :, None], d, axis=3)
+    else:
+        gate = _decode_bf16(w.gate) if w.gate is not None else None
     lens = w.seqlens if s.layout != "ragged" else np.diff(w.cu_seqlens)
     inv = _inverse_rows(w)
     mult = None

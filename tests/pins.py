@@ -65,10 +65,18 @@ def check_head_map_truth_table():
     assert rows == 4
 
 
-def check_brute(spec, seed=0, atol=1e-12):
+def check_brute(spec, seed=0, atol=1e-12, softmax_scale=None, gate_mode="elementwise"):
+    """Oracle against the brute force on one tiny workload.  A headwise gate
+    takes each head's first gate value ([B, S_q, H_q])."""
     w = gi.build(spec, seed)
-    O, L = run_oracle(w)
-    Ob, Lb = brute_decode(w)
+    if gate_mode == "headwise":
+        hw = np.ascontiguousarray(w.gate[..., 0])
+        O, L = R.reference_decode(**dict(w.arrays(), gate=hw), **w.params(), gate_mode="headwise",
+                                  softmax_scale=softmax_scale)
+        Ob, Lb = brute_decode(w, softmax_scale=softmax_scale, headwise_gate=hw)
+    else:
+        O, L = run_oracle(w, softmax_scale=softmax_scale)
+        Ob, Lb = brute_decode(w, softmax_scale=softmax_scale)
     assert np.array_equal(np.isneginf(L), np.isneginf(Lb))
     fin = np.isfinite(Lb)
     assert np.allclose(L[fin], Lb[fin], rtol=0, atol=atol), np.abs(L[fin] - Lb[fin]).max()
@@ -294,6 +302,24 @@ ALL_CHECKS = [
     ("brute_sparse_masked", lambda: check_brute(tiny_spec(layout="paged", lengths=(9, 14), page_size=4, topk=12, topk_mode="random_masked"))),
     ("brute_gate", lambda: check_brute(tiny_spec(lengths=(4, 7), gate=True))),
     ("brute_fp8", check_fp8_brute),
+    # a given softmax scale, positive and negative ("Sparse paged GQA decode
+    # attention with FP8 KV cache on SM89", "Implementations": one folded
+    # score multiplier), on causal, paged top-K and FP8 cases
+    ("brute_scale_0.3_causal", lambda: check_brute(tiny_spec(h_q=8, h_kv=2, s_q=2, causal=True, lengths=(6, 9)),
+                                                   seed=16, softmax_scale=0.3)),
+    ("brute_scale_neg_fp8_sparse", lambda: check_brute(tiny_spec(layout="paged", lengths=(16, 13), page_size=4,
+                                                                 kv_dtype="fp8_e4m3fn", topk=16,
+                                                                 topk_mode="random_masked", gate=True),
+                                                       seed=17, softmax_scale=-0.11)),
+    # a headwise gate [B, S_q, H_q] (same page, "Workload": sigmoid gate
+    # after attention), with S_q > 1 so that its two leading axes cannot be
+    # confused, bf16 and FP8
+    ("brute_headwise_gate_causal", lambda: check_brute(tiny_spec(h_q=8, h_kv=2, s_q=3, causal=True, gate=True,
+                                                                 lengths=(7, 4)), seed=18, gate_mode="headwise")),
+    ("brute_headwise_gate_fp8_scale", lambda: check_brute(tiny_spec(layout="paged", h_q=4, h_kv=2, s_q=2,
+                                                                    causal=True, gate=True, lengths=(9, 12),
+                                                                    page_size=4, kv_dtype="fp8_e4m3fn"),
+                                                          seed=19, gate_mode="headwise", softmax_scale=0.21)),
     ("gqa_equals_mha_8x4", lambda: check_gqa_equals_mha(tiny_spec(h_q=8, h_kv=4))),
     ("gqa_equals_mha_8x2", lambda: check_gqa_equals_mha(tiny_spec(h_q=8, h_kv=2))),
     ("gqa_equals_mha_8x1", lambda: check_gqa_equals_mha(tiny_spec(h_q=8, h_kv=1))),

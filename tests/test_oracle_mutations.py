@@ -17,6 +17,8 @@ import pins
 _orig_softmax = R.softmax_attend
 _orig_phys = R.physical_row
 _orig_vis = R.visible_positions
+_orig_scale = R.score_scale
+_orig_gate = R.gate_factor
 
 
 def _lse_without_max(q, K, V, scale):
@@ -81,6 +83,28 @@ def _int8_unsigned(codes):
     return np.asarray(codes, dtype=np.uint8).astype(np.float64)   # sign ignored
 
 
+def _scale_ignored(head_dim, softmax_scale=None):
+    return 1.0 / math.sqrt(head_dim)                # the caller's scale dropped
+
+
+def _scale_abs(head_dim, softmax_scale=None):
+    return abs(_orig_scale(head_dim, softmax_scale))  # sign of a given scale dropped
+
+
+def _headwise_gate_b_h_i(gate, gate_mode, b, i, h):
+    if gate_mode == "headwise":
+        B, Sq, Hq = gate.shape
+        flat = np.asarray(gate).reshape(B, Hq, Sq)    # read as [B, H_q, S_q]
+        return R.sigmoid(R.bf16_bits_to_f64(flat[b, h, i]))
+    return _orig_gate(gate, gate_mode, b, i, h)
+
+
+def _headwise_gate_skipped(gate, gate_mode, b, i, h):
+    if gate_mode == "headwise":
+        return 1.0                                    # only the elementwise gate applied
+    return _orig_gate(gate, gate_mode, b, i, h)
+
+
 MUTATIONS = {
     "kv_head_(h//Hkv)%Hkv": ("kv_head", lambda h, hq, hkv: (h // hkv) % hkv),
     "kv_head_h//Hkv": ("kv_head", lambda h, hq, hkv: min(h // hkv, hkv - 1)),
@@ -94,6 +118,10 @@ MUTATIONS = {
     "fp8_exponent_bias_8": ("e4m3fn_value", _fp8_bias8),
     "bf16_decode_shift_15": ("bf16_bits_to_f64", _bf16_wrong_shift),
     "int8_read_unsigned": ("int8_codes_to_f64", _int8_unsigned),
+    "softmax_scale_ignored": ("score_scale", _scale_ignored),
+    "softmax_scale_sign_dropped": ("score_scale", _scale_abs),
+    "headwise_gate_read_b_h_i": ("gate_factor", _headwise_gate_b_h_i),
+    "headwise_gate_not_applied": ("gate_factor", _headwise_gate_skipped),
 }
 
 
