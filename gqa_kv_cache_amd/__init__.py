@@ -166,12 +166,70 @@ def gqa_decode_workspace_size(params: Params) -> int:
     return int(n.value)
 
 
-def _ptr(x):
-    if x is None:
-        return None
-    if isinstance(x, int):
-        return x
-    return x.data_ptr()
+# Element types each tensor argument may have.  Raw bit containers are
+# accepted for stored bf16 values (int16 / uint16 views of the bits) and for
+# one-byte codes (uint8 / int8 bytes); index arrays, scales and LSE must be
+# exactly the type the kernels read.
+def _dtypes(kind: str):
+    import torch
+    bits16 = tuple(t for t in (torch.bfloat16, torch.int16, getattr(torch, "uint16", None)) if t is not None)
+    fp8 = getattr(torch, "float8_e4m3fn", None)
+    return {
+        "bf16": (torch.bfloat16,),
+        "bf16_bits": bits16,
+        "fp8_codes": tuple(t for t in (torch.uint8, torch.int8, fp8) if t is not None),
+        "int8_codes": (torch.int8, torch.uint8),
+        "int32": (torch.int32,),
+        "int64": (torch.int64,),
+        "float32": (torch.float32,),
+    }[kind]
+
+
+def _cache_kind(kv_dtype: int) -> str:
+    return {KV_BF16: "bf16_bits", KV_FP8_E4M3FN: "fp8_codes", KV_INT8: "int8_codes"}.get(kv_dtype, "bf16_bits")
+
+
+class _Checked:
+    """Checks what the C ABI cannot see in a plain pointer: each tensor's
+    element type, that it is contiguous, its size, and that every tensor
+    sits on one CUDA device.  An int is taken as a raw device pointer and
+    passed on unchecked.  Failures raise GqaError(GQA_ERR_INVALID_ARG)
+    before anything reaches the library."""
+
+    def __init__(self):
+        self.devices = {}
+
+    def ptr(self, x, name: str, kind: Optional[str] = None, *, exact: Optional[int] = None,
+            at_least: Optional[int] = None, min_bytes: Optional[int] = None):
+        if x is None or isinstance(x, int):
+            return x
+        import torch
+        if not isinstance(x, torch.Tensor):
+            raise GqaError(1, f"{name}: expected a torch tensor or an int device pointer, not {type(x).__name__}")
+        if kind is not None and x.dtype not in _dtypes(kind):
+            raise GqaError(1, f"{name}: dtype {x.dtype} is not one of {[str(t) for t in _dtypes(kind)]}")
+        if not x.is_contiguous():
+            raise GqaError(1, f"{name}: tensor is not contiguous")
+        if exact is not None and x.numel() != exact:
+            raise GqaError(1, f"{name}: {x.numel()} elements, expected {exact}")
+        if at_least is not None and x.numel() < at_least:
+            raise GqaError(1, f"{name}: {x.numel()} elements, at least {at_least} needed")
+        if min_bytes is not None and x.numel() * x.element_size() < min_bytes:
+            raise GqaError(1, f"{name}: {x.numel() * x.element_size()} bytes, at least {min_bytes} needed")
+        self.devices[name] = x.device
+        return x.data_ptr()
+
+    def same_cuda_device(self):
+        devs = set(self.devices.values())
+        for name, d in self.devices.items():
+            if d.type != "cuda":
+                raise GqaError(1, f"{name}: tensor is on {d}, not on a CUDA device")
+        if len(devs) > 1:
+            raise GqaError(1, f"tensors are on different devices: {sorted(str(d) for d in devs)}")
+
+
+def _nbytes(x) -> int:
+    return x.numel() * x.element_size()
 
 
 def _stream_handle(stream):
@@ -188,23 +246,55 @@ def gqa_decode_run(params: Params, q, k_cache, v_cache, seqlens=None, cu_seqlens
                    o=None, lse=None, workspace=None, workspace_bytes: Optional[int] = None,
                    stream=None) -> None:
     """Enqueue one decode call.  Tensors are passed by device pointer; the
-    caller keeps them alive until the stream has run the call."""
-    lib = load_library()
+    caller keeps them alive until the stream has run the call.  Tensor
+    arguments are checked first (element type, contiguity, size, one CUDA
+    device); an int is a raw device pointer, passed on as it is.
+    workspace_bytes defaults to the workspace tensor's own size; an int
+    workspace pointer needs it given."""
+    p = params
+    B, Sq, Hq, Hkv, d = p.batch, p.s_q, p.h_q, p.h_kv, p.head_dim
+    esz = 2 if p.kv_dtype == KV_BF16 else 1
+    c = _Checked()
+    args = [
+        c.ptr(q, "q", "bf16", exact=B * Sq * Hq * d),
+        c.ptr(k_cache, "k_cache", _cache_kind(p.kv_dtype), min_bytes=p.kv_rows * Hkv * d * esz),
+        c.ptr(v_cache, "v_cache", _cache_kind(p.kv_dtype), min_bytes=p.kv_rows * Hkv * d * esz),
+        c.ptr(seqlens, "seqlens", "int32", at_least=B),
+        c.ptr(cu_seqlens, "cu_seqlens", "int32", at_least=B + 1),
+        c.ptr(block_table, "block_table", "int32", at_least=B * p.max_pages_per_seq),
+        c.ptr(topk_idx, "topk_idx", "int32", at_least=B * p.topk),
+        c.ptr(k_scale, "k_scale", "float32", at_least=B * Hkv),
+        c.ptr(v_scale, "v_scale", "float32", at_least=B * Hkv),
+        c.ptr(gate, "gate", "bf16", exact=B * Sq * Hq * (1 if p.gate_mode == GATE_HEADWISE else d)),
+        c.ptr(o, "o", "bf16", exact=B * Sq * Hq * d),
+        c.ptr(lse, "lse", "float32", exact=B * Hq * Sq),
+        c.ptr(workspace, "workspace"),
+    ]
+    c.same_cuda_device()
     if workspace_bytes is None:
-        workspace_bytes = 0 if workspace is None else (
-            workspace.numel() * workspace.element_size() if not isinstance(workspace, int) else 0)
-    st = lib.gqa_decode_run(ctypes.byref(params), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens),
-                            _ptr(cu_seqlens), _ptr(block_table), _ptr(topk_idx), _ptr(k_scale),
-                            _ptr(v_scale), _ptr(gate), _ptr(o), _ptr(lse), _ptr(workspace),
-                            ctypes.c_size_t(workspace_bytes), _stream_handle(stream))
+        if isinstance(workspace, int):
+            raise GqaError(1, "an int workspace pointer needs workspace_bytes")
+        workspace_bytes = 0 if workspace is None else _nbytes(workspace)
+    lib = load_library()
+    st = lib.gqa_decode_run(ctypes.byref(params), *args, ctypes.c_size_t(workspace_bytes), _stream_handle(stream))
     _check(lib, st)
 
 
 def gqa_resolve_rows(params: Params, seqlens=None, cu_seqlens=None, block_table=None,
                      topk_idx=None, rows_out=None, stream=None) -> None:
+    p = params
+    B = p.batch
+    c = _Checked()
+    args = [
+        c.ptr(seqlens, "seqlens", "int32", at_least=B),
+        c.ptr(cu_seqlens, "cu_seqlens", "int32", at_least=B + 1),
+        c.ptr(block_table, "block_table", "int32", at_least=B * p.max_pages_per_seq),
+        c.ptr(topk_idx, "topk_idx", "int32", at_least=B * p.topk),
+        c.ptr(rows_out, "rows_out", "int64", exact=B * p.s_q * (p.topk if p.topk > 0 else p.max_seqlen_kv)),
+    ]
+    c.same_cuda_device()
     lib = load_library()
-    st = lib.gqa_resolve_rows(ctypes.byref(params), _ptr(seqlens), _ptr(cu_seqlens), _ptr(block_table),
-                              _ptr(topk_idx), _ptr(rows_out), _stream_handle(stream))
+    st = lib.gqa_resolve_rows(ctypes.byref(params), *args, _stream_handle(stream))
     _check(lib, st)
 
 
@@ -233,14 +323,31 @@ def gqa_kv_append_workspace_size(params: AppendParams) -> int:
 def gqa_kv_append(params: AppendParams, k_new, v_new, seqlens, seqlens_out=None, block_table=None,
                   k_cache=None, v_cache=None, k_scale=None, v_scale=None, workspace=None,
                   workspace_bytes: Optional[int] = None, stream=None) -> None:
-    """Enqueue one append: the new rows go after each request's length."""
-    lib = load_library()
+    """Enqueue one append: the new rows go after each request's length.
+    Tensor arguments are checked as in gqa_decode_run."""
+    p = params
+    B, S, Hkv, d = p.batch, p.s_new, p.h_kv, p.head_dim
+    esz = 2 if p.kv_dtype == KV_BF16 else 1
+    c = _Checked()
+    args = [
+        c.ptr(k_new, "k_new", "bf16_bits", exact=B * S * Hkv * d),
+        c.ptr(v_new, "v_new", "bf16_bits", exact=B * S * Hkv * d),
+        c.ptr(seqlens, "seqlens", "int32", at_least=B),
+        c.ptr(seqlens_out, "seqlens_out", "int32", at_least=B),
+        c.ptr(block_table, "block_table", "int32", at_least=B * p.max_pages_per_seq),
+        c.ptr(k_cache, "k_cache", _cache_kind(p.kv_dtype), min_bytes=p.kv_rows * Hkv * d * esz),
+        c.ptr(v_cache, "v_cache", _cache_kind(p.kv_dtype), min_bytes=p.kv_rows * Hkv * d * esz),
+        c.ptr(k_scale, "k_scale", "float32", at_least=B * Hkv),
+        c.ptr(v_scale, "v_scale", "float32", at_least=B * Hkv),
+        c.ptr(workspace, "workspace"),
+    ]
+    c.same_cuda_device()
     if workspace_bytes is None:
-        workspace_bytes = 0 if workspace is None else (
-            workspace.numel() * workspace.element_size() if not isinstance(workspace, int) else 0)
-    st = lib.gqa_kv_append(ctypes.byref(params), _ptr(k_new), _ptr(v_new), _ptr(seqlens), _ptr(seqlens_out),
-                           _ptr(block_table), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
-                           _ptr(workspace), ctypes.c_size_t(workspace_bytes), _stream_handle(stream))
+        if isinstance(workspace, int):
+            raise GqaError(1, "an int workspace pointer needs workspace_bytes")
+        workspace_bytes = 0 if workspace is None else _nbytes(workspace)
+    lib = load_library()
+    st = lib.gqa_kv_append(ctypes.byref(params), *args, ctypes.c_size_t(workspace_bytes), _stream_handle(stream))
     _check(lib, st)
 
 
@@ -303,6 +410,7 @@ def decode(q, k_cache, v_cache, *, h_kv: Optional[int] = None, seqlens=None, cu_
     ws = gqa_decode_workspace_size(params)
     if ws and workspace is None:
         workspace = torch.empty(ws, dtype=torch.uint8, device=dev)
+    # the workspace's own size: the library rejects one that is too small
     gqa_decode_run(params, q, k_cache, v_cache, seqlens, cu_seqlens, block_table, topk_idx, k_scale,
-                   v_scale, gate, out, lse, workspace, ws if workspace is not None else 0, stream)
+                   v_scale, gate, out, lse, workspace, None if workspace is not None else 0, stream)
     return out, lse

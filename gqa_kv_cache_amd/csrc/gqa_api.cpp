@@ -23,7 +23,6 @@ hipError_t launch_partial(const DecodeArgs& a, int D, int kvt, int mode, int mb,
                           hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_combine(const DecodeArgs& a, int D, dim3 grid, hipStream_t st);
 hipError_t launch_resolve(const DecodeArgs& a, int64_t* out, int list_cap, hipStream_t st);
-size_t partial_lds_bytes(int D, bool fp8, bool indirect, int chunk);
 }  // namespace gqa
 
 namespace {
@@ -147,14 +146,23 @@ static_assert(GQA_KV_BF16 == gqa::kKvBf16 && GQA_KV_FP8_E4M3FN == gqa::kKvFp8 &&
 
 bool packed_mode(const gqa_decode_params* p) { return p->layout == GQA_LAYOUT_RAGGED && p->topk == 0; }
 
+// Largest workspace a plan may ask for.  Shapes whose split partials would
+// exceed it (no device holds them) are rejected instead of having their
+// byte count wrap.
+constexpr unsigned __int128 kMaxWorkspaceBytes = (unsigned __int128)1 << 40;
+
 // Bytes of the fp32 partial outputs (the LSE partials follow, rounded up to
 // 256 bytes): (request, KV head, split) slots of rows x head_dim each; packed
-// chunks use slots (request + chunk, KV head).
-size_t partial_o_bytes(const gqa_decode_params* p, const gqa_decode_plan& plan) {
-  const int64_t slots = packed_mode(p) ? ((int64_t)p->batch + plan.num_splits - 1) * p->h_kv
-                                       : (int64_t)p->batch * p->h_kv * plan.num_splits;
-  return (size_t)slots * plan.rows * p->head_dim * sizeof(float);
+// chunks use slots (request + chunk, KV head).  Exact in 128 bits: every
+// factor is below 2^32.
+unsigned __int128 partial_o_bytes(const gqa_decode_params* p, const gqa_decode_plan& plan) {
+  const unsigned __int128 slots = packed_mode(p)
+                                      ? ((unsigned __int128)p->batch + plan.num_splits - 1) * (unsigned)p->h_kv
+                                      : (unsigned __int128)p->batch * (unsigned)p->h_kv * (unsigned)plan.num_splits;
+  return slots * (unsigned)plan.rows * (unsigned)p->head_dim * sizeof(float);
 }
+
+unsigned __int128 round_up_256(unsigned __int128 x) { return (x + 255) / 256 * 256; }
 
 // The math path GQA_MATH_AUTO takes for a group of `rows` query rows.
 // Measured on MI355X over 128K-token decodes (bf16 d = 128 and 64, FP8
@@ -299,9 +307,12 @@ gqa_status make_plan(const gqa_decode_params* p, gqa_decode_plan* plan) {
   // also writes the empty requests; partial slots are (request + chunk).
   plan->combine = (packed || splits > 1) ? 1 : 0;
   if (plan->combine) {
-    const size_t opart = partial_o_bytes(p, *plan);
-    const size_t lpart = opart / p->head_dim;
-    plan->workspace_bytes = round_up(opart, 256) + round_up(lpart, 256);
+    const unsigned __int128 opart = partial_o_bytes(p, *plan);
+    const unsigned __int128 ws = round_up_256(opart) + round_up_256(opart / p->head_dim);
+    if (ws > kMaxWorkspaceBytes)
+      return fail(GQA_ERR_UNSUPPORTED, "the split partials would need %.3g bytes of workspace (limit 2^40)",
+                  (double)ws);
+    plan->workspace_bytes = (size_t)ws;
   }
   return GQA_OK;
 }
@@ -375,7 +386,8 @@ void fill_args(gqa::DecodeArgs& a, const gqa_decode_params* p, const gqa_decode_
 
 gqa_status check_append(const gqa_append_params* p) {
   if (!p) return fail(GQA_ERR_INVALID_ARG, "params is NULL");
-  if (p->batch < 0 || p->s_new < 1) return fail(GQA_ERR_INVALID_ARG, "batch must be >= 0 and s_new >= 1");
+  if (p->batch < 0 || p->batch > 65535 || p->s_new < 1)
+    return fail(GQA_ERR_INVALID_ARG, "batch must be in [0, 65535] and s_new >= 1");  // batch is grid.y
   if (p->h_kv < 1 || p->h_kv > gqa::kAppendMaxHeads)
     return fail(GQA_ERR_UNSUPPORTED, "h_kv must be 1..%d", gqa::kAppendMaxHeads);
   if (p->head_dim != 64 && p->head_dim != 128 && p->head_dim != 256)
@@ -500,7 +512,7 @@ gqa_status gqa_decode_run(const gqa_decode_params* p, const void* q, const void*
   a.lse = lse;
   if (plan.workspace_bytes > 0) {
     a.o_part = static_cast<float*>(workspace);
-    a.lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + round_up(partial_o_bytes(p, plan), 256));
+    a.lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + (size_t)round_up_256(partial_o_bytes(p, plan)));
   }
 
   hipStream_t s = static_cast<hipStream_t>(stream);

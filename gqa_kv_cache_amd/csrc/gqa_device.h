@@ -51,6 +51,20 @@ __host__ __device__ constexpr int partial_wgs_per_cu(int D, bool fp8, int mb, in
 }
 constexpr int kPThreads = 64 * kPWaves;
 
+// Shared memory of the partial kernel: per wave a K tile (raw 16-byte
+// chunks) and a V tile (bf16), statically allocated; after the tile loop
+// the same space holds the waves' fp32 accumulators.  The dynamic part
+// holds the resolved row table of paged / top-K chunks.
+__host__ __device__ constexpr int ktile_chunks(int D, bool fp8) { return kTile * D * (fp8 ? 1 : 2) / 16; }
+__host__ __device__ constexpr int vtile_elems(int D) { return kTile * D; }
+__host__ __device__ constexpr int wave_tile_bytes(int D, bool fp8) { return ktile_chunks(D, fp8) * 16 + vtile_elems(D) * 2; }
+__host__ __device__ constexpr size_t table_bytes(bool indirect, int chunk) { return indirect ? (size_t)chunk * 8 : 0; }
+// LDS bytes of one partial workgroup: the tiles, the merge statistics and
+// the row table.
+__host__ __device__ constexpr size_t partial_lds_bytes(int D, bool fp8, bool indirect, int chunk) {
+  return (size_t)kPWaves * wave_tile_bytes(D, fp8) + 2 * kPWaves * 16 * 4 + table_bytes(indirect, chunk);
+}
+
 // Everything a kernel needs, passed by value (kernarg segment).
 struct DecodeArgs {
   const uint16_t* q;          // bf16 [B, S_q, H_q, D]

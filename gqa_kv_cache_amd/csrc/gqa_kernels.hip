@@ -63,15 +63,6 @@ struct TileShape {
   static constexpr int NLDP = NLD / NPART;    // wave-wide loads per part per tensor
 };
 
-// Shared memory of the partial kernel: per wave a K tile (raw 16-byte
-// chunks) and a V tile (bf16), statically allocated; after the tile loop
-// the same space holds the waves' fp32 accumulators.  The dynamic part
-// holds the resolved row table of paged / top-K chunks.
-__host__ __device__ constexpr int ktile_chunks(int D, bool fp8) { return kTile * D * (fp8 ? 1 : 2) / 16; }
-__host__ __device__ constexpr int vtile_elems(int D) { return kTile * D; }
-__host__ __device__ constexpr int wave_tile_bytes(int D, bool fp8) { return ktile_chunks(D, fp8) * 16 + vtile_elems(D) * 2; }
-__host__ __device__ constexpr size_t table_bytes(bool indirect, int chunk) { return indirect ? (size_t)chunk * 8 : 0; }
-
 // Contraction slot -> d.  K-step kk, lane group qd covers d = qk_d(kk, qd)
 // .. +7.  bf16: one 16-byte chunk per k-step (chunk 4 kk + qd); FP8: one
 // 16-byte chunk (16 codes, chunk 4 (kk / 2) + qd) feeds two k-steps.
@@ -1196,10 +1187,6 @@ static hipError_t launch_mode(const DecodeArgs& a, int mode, int mb, int rv, int
     case kPacked: return launch_mb<D, KVT, kPacked>(a, mb, rv, share, grid, st, ev0, ev1);
     default: return launch_mb<D, KVT, kDense>(a, mb, rv, share, grid, st, ev0, ev1);
   }
-}
-
-size_t partial_lds_bytes(int D, bool fp8, bool indirect, int chunk) {
-  return (size_t)kPWaves * wave_tile_bytes(D, fp8) + 2 * kPWaves * 16 * 4 + table_bytes(indirect, chunk);
 }
 
 template <int D>

@@ -54,7 +54,7 @@ extern "C" {
 enum { GQA_SCALE_GIVEN = 0, GQA_SCALE_FIRST_BLOCK = 1 };
 
 typedef struct gqa_append_params {
-  int32_t batch;             /* B >= 0                                                  */
+  int32_t batch;             /* 0 <= B <= 65535                                         */
   int32_t s_new;             /* rows appended per request, >= 1                         */
   int32_t h_kv;              /* KV heads, 1..256                                        */
   int32_t head_dim;          /* 64, 128 or 256                                          */

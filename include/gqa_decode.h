@@ -97,7 +97,7 @@ enum { GQA_GATE_NONE = 0, GQA_GATE_ELEMENTWISE = 1, GQA_GATE_HEADWISE = 2 };
 enum { GQA_MATH_AUTO = 0, GQA_MATH_MFMA = 1, GQA_MATH_VALU = 2 };
 
 typedef struct gqa_decode_params {
-  int32_t batch;             /* B >= 0                                                  */
+  int32_t batch;             /* 0 <= B <= 65535                                         */
   int32_t s_q;               /* query tokens per request, 1..64                         */
   int32_t h_q;               /* query heads                                             */
   int32_t h_kv;              /* KV heads; h_q % h_kv == 0, (h_q/h_kv)*s_q <= 512        */
@@ -146,7 +146,14 @@ gqa_status gqa_decode_make_plan(const gqa_decode_params* p, gqa_decode_plan* pla
 
 /* Workspace bytes gqa_decode_run needs for *p: the split partials
  * (num_splits * rows * (head_dim + 1) fp32 per (request, KV head)), 0 when
- * one split covers every list.                                              */
+ * one split covers every list.  The KV walk is split across workgroups
+ * (an unsplit walk is one of the causes of slow decode named in "When the
+ * K/V copy costs more than the attention", section "What I was looking
+ * at"), and each split leaves an output row and its log-sum-exp here for
+ * the combine.  The workspace never holds K or V expanded to H_q heads:
+ * that expansion is what ran out of memory on the same page ("What it did,
+ * and what it didn't").  Shapes whose partials would exceed 2^40 bytes are
+ * rejected with GQA_ERR_UNSUPPORTED.                                       */
 gqa_status gqa_decode_workspace_size(const gqa_decode_params* p, size_t* bytes);
 
 /* Decode attention.
@@ -179,7 +186,12 @@ gqa_status gqa_decode_run(const gqa_decode_params* p,
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /* Address resolution on the device, with the same code the decode kernels
- * use to turn (request, list slot) into a physical token row.
+ * use to turn (request, list slot) into a physical token row: a top-K
+ * entry names a token of the request, and a page of page_size tokens found
+ * through the request's block-table row holds it ("Sparse paged GQA decode
+ * attention with FP8 KV cache on SM89", section "Workload": top-K 512 token
+ * indices, pages of 16, 32 pages per request; section "Implementations":
+ * the eager version gathers the selected K/V rows before attending).
  * rows_out: int64 [B, S_q, list_len], list_len = topk if topk > 0 else
  * max_seqlen_kv; entry = physical token row of that slot for query i, or -1
  * where the slot is masked (beyond n_b, outside [0, n_b) for a top-K entry,
