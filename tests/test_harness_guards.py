@@ -61,13 +61,16 @@ def test_bench_check_flags_nan():
     sys.path.insert(0, ROOT)
     import bench
     Oref, Lref = _reference(rows=4, d=8)
-    rows = [(0, 0, h) for h in range(4)]
+    rows = np.array([(0, 0, h) for h in range(4)], np.int64)     # (b, i, h) of each oracle row
+    Orows, Lrows = Oref[0, 0], Lref[0, :, 0]                        # [4, d] and [4]
     o = torch.from_numpy(Oref.astype(np.float32))
     o[0, 0, 2, 1] = float("nan")
     lse = torch.from_numpy(Lref.astype(np.float32))
-    assert bench.check_against_oracle(o, lse, rows, Oref, Lref, False)["ok"] is False
-    assert bench.check_against_oracle(torch.from_numpy(Oref.astype(np.float32)), lse, rows, Oref, Lref,
-                                      False)["ok"] is True
+    assert bench.check_against_oracle(o, lse, rows, Orows, Lrows, False)["ok"] is False
+    good = torch.from_numpy(Oref.astype(np.float32))
+    assert bench.check_against_oracle(good, lse, rows, Orows, Lrows, False)["ok"] is True
+    assert bench.check_against_oracle(torch.zeros_like(good), lse, rows, Orows, Lrows, False)["ok"] is False
+    assert bench.check_against_oracle(good, lse, rows[:0], Orows[:0], Lrows[:0], False)["ok"] is False
 
 
 def test_bench_refuses_more_than_one_gpu():
