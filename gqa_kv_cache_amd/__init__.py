@@ -8,6 +8,7 @@ and ``include/gqa_append.h``:
     gqa_decode_make_plan(params)              -> dict
     gqa_decode_workspace_size(params)         -> int
     gqa_decode_run(params, q, k_cache, ...)   -> None (writes o, lse)
+    gqa_decode_run_noalloc(params, q, ...)    -> None (no workspace; library scratch)
     gqa_resolve_rows(params, ..., rows_out)   -> None
     gqa_kv_append_workspace_size(aparams)     -> int
     gqa_kv_append(aparams, k_new, v_new, ...) -> None (writes the cache rows)
@@ -96,11 +97,13 @@ def load_library(path: Optional[str] = None):
     lib.gqa_decode_make_plan.argtypes = [P, ctypes.POINTER(Plan)]
     lib.gqa_decode_workspace_size.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
     lib.gqa_decode_run.argtypes = [P] + [vp] * 13 + [ctypes.c_size_t, vp]
+    lib.gqa_decode_run_noalloc.argtypes = [P] + [vp] * 12 + [vp]
     lib.gqa_resolve_rows.argtypes = [P, vp, vp, vp, vp, vp, vp]
     A = ctypes.POINTER(AppendParams)
     lib.gqa_kv_append_workspace_size.argtypes = [A, ctypes.POINTER(ctypes.c_size_t)]
     lib.gqa_kv_append.argtypes = [A] + [vp] * 10 + [ctypes.c_size_t, vp]
-    for f in ("gqa_decode_make_plan", "gqa_decode_workspace_size", "gqa_decode_run", "gqa_resolve_rows",
+    for f in ("gqa_decode_make_plan", "gqa_decode_workspace_size", "gqa_decode_run", "gqa_decode_run_noalloc",
+              "gqa_resolve_rows",
               "gqa_kv_append_workspace_size", "gqa_kv_append"):
         getattr(lib, f).restype = ctypes.c_int
     lib.gqa_status_string.argtypes = [ctypes.c_int]
@@ -277,6 +280,40 @@ def gqa_decode_run(params: Params, q, k_cache, v_cache, seqlens=None, cu_seqlens
         workspace_bytes = 0 if workspace is None else _nbytes(workspace)
     lib = load_library()
     st = lib.gqa_decode_run(ctypes.byref(params), *args, ctypes.c_size_t(workspace_bytes), _stream_handle(stream))
+    _check(lib, st)
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20   # GQA_NOALLOC_SCRATCH_BYTES
+
+
+def gqa_decode_run_noalloc(params: Params, q, k_cache, v_cache, seqlens=None, cu_seqlens=None,
+                           block_table=None, topk_idx=None, k_scale=None, v_scale=None, gate=None,
+                           o=None, lse=None, stream=None) -> None:
+    """gqa_decode_run without a workspace: the split partials go to the
+    library's per-device scratch array (at most NOALLOC_SCRATCH_BYTES; a
+    larger plan raises GQA_ERR_WORKSPACE).  Calls that overlap on one
+    device share that array and must be ordered by the caller."""
+    p = params
+    B, Sq, Hq, Hkv, d = p.batch, p.s_q, p.h_q, p.h_kv, p.head_dim
+    esz = 2 if p.kv_dtype == KV_BF16 else 1
+    c = _Checked()
+    args = [
+        c.ptr(q, "q", "bf16", exact=B * Sq * Hq * d),
+        c.ptr(k_cache, "k_cache", _cache_kind(p.kv_dtype), min_bytes=p.kv_rows * Hkv * d * esz),
+        c.ptr(v_cache, "v_cache", _cache_kind(p.kv_dtype), min_bytes=p.kv_rows * Hkv * d * esz),
+        c.ptr(seqlens, "seqlens", "int32", at_least=B),
+        c.ptr(cu_seqlens, "cu_seqlens", "int32", at_least=B + 1),
+        c.ptr(block_table, "block_table", "int32", at_least=B * p.max_pages_per_seq),
+        c.ptr(topk_idx, "topk_idx", "int32", at_least=B * p.topk),
+        c.ptr(k_scale, "k_scale", "float32", at_least=B * Hkv),
+        c.ptr(v_scale, "v_scale", "float32", at_least=B * Hkv),
+        c.ptr(gate, "gate", "bf16", exact=B * Sq * Hq * (1 if p.gate_mode == GATE_HEADWISE else d)),
+        c.ptr(o, "o", "bf16", exact=B * Sq * Hq * d),
+        c.ptr(lse, "lse", "float32", exact=B * Hq * Sq),
+    ]
+    c.same_cuda_device()
+    lib = load_library()
+    st = lib.gqa_decode_run_noalloc(ctypes.byref(params), *args, _stream_handle(stream))
     _check(lib, st)
 
 

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libgqa_decode.so")
-SOURCES = ["gqa_kernels.hip", "gqa_append.hip", "gqa_api.cpp"]
+SOURCES = ["gqa_kernels.hip", "gqa_append.hip", "gqa_scratch.hip", "gqa_api.cpp"]
 ARCH = "gfx950"
 
 

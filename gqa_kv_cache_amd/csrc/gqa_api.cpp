@@ -23,6 +23,7 @@ hipError_t launch_partial(const DecodeArgs& a, int D, int kvt, int mode, int mb,
                           hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_combine(const DecodeArgs& a, int D, dim3 grid, hipStream_t st);
 hipError_t launch_resolve(const DecodeArgs& a, int64_t* out, int list_cap, hipStream_t st);
+hipError_t scratch_address(void** ptr, size_t* bytes);
 }  // namespace gqa
 
 namespace {
@@ -533,6 +534,29 @@ gqa_status gqa_decode_run(const gqa_decode_params* p, const void* q, const void*
     if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
   }
   return GQA_OK;
+}
+
+gqa_status gqa_decode_run_noalloc(const gqa_decode_params* p, const void* q, const void* k_cache,
+                                  const void* v_cache, const int32_t* seqlens, const int32_t* cu_seqlens,
+                                  const int32_t* block_table, const int32_t* topk_idx, const float* k_scale,
+                                  const float* v_scale, const void* gate, void* o, float* lse, void* stream) {
+  g_last_error.clear();
+  gqa_decode_plan plan;
+  gqa_status st = make_plan(p, &plan);
+  if (st != GQA_OK) return st;
+  if (plan.workspace_bytes > GQA_NOALLOC_SCRATCH_BYTES)
+    return fail(GQA_ERR_WORKSPACE, "this call needs %zu bytes of split partials; the no-allocation entry point "
+                "holds %zu (use gqa_decode_run with a workspace)", plan.workspace_bytes,
+                (size_t)GQA_NOALLOC_SCRATCH_BYTES);
+  void* scratch = nullptr;
+  size_t scratch_bytes = 0;
+  if (plan.workspace_bytes > 0) {
+    const hipError_t e = gqa::scratch_address(&scratch, &scratch_bytes);
+    if (e != hipSuccess) return hip_fail(e, "scratch array address");
+  }
+  // The same checks and launches as a call with a caller workspace.
+  return gqa_decode_run(p, q, k_cache, v_cache, seqlens, cu_seqlens, block_table, topk_idx, k_scale, v_scale, gate,
+                        o, lse, scratch, scratch_bytes, stream);
 }
 
 gqa_status gqa_resolve_rows(const gqa_decode_params* p, const int32_t* seqlens, const int32_t* cu_seqlens,

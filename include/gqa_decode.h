@@ -185,6 +185,31 @@ gqa_status gqa_decode_run(const gqa_decode_params* p,
                           const void* gate, void* o, float* lse,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of the scratch array gqa_decode_run_noalloc keeps on each device. */
+#define GQA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/* Decode attention with no caller workspace, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Same arguments (less the
+ * workspace), checks, kernels and results as gqa_decode_run.  The split
+ * partials go to a scratch array of GQA_NOALLOC_SCRATCH_BYTES that the
+ * library holds on each device it runs on, from the first call on that
+ * device until the process ends; no call allocates or frees memory.
+ *   - A call whose plan needs more workspace than the array holds (see
+ *     gqa_decode_workspace_size) returns GQA_ERR_WORKSPACE and enqueues
+ *     nothing.
+ *   - Every call on one device uses that device's one array: calls that
+ *     may overlap on one device (several streams, several host threads)
+ *     race on it, and the caller must order them.
+ *   - The scratch needs no initialisation and holds nothing a later call
+ *     reads.                                                              */
+gqa_status gqa_decode_run_noalloc(const gqa_decode_params* p,
+                                  const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* seqlens, const int32_t* cu_seqlens,
+                                  const int32_t* block_table, const int32_t* topk_idx,
+                                  const float* k_scale, const float* v_scale,
+                                  const void* gate, void* o, float* lse, void* stream);
+
 /* Address resolution on the device, with the same code the decode kernels
  * use to turn (request, list slot) into a physical token row: a top-K
  * entry names a token of the request, and a page of page_size tokens found

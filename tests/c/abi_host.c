@@ -62,6 +62,17 @@ int main(void) {
                        0, NULL) == GQA_ERR_INVALID_ARG,
         "run without q rejected");
 
+  /* the no-allocation entry point refuses a plan whose split partials
+   * exceed its scratch array before it touches a device (64 query tokens of
+   * 64/8 heads over 128K tokens: 512 rows per KV head) */
+  p.s_q = 64;
+  CHECK(gqa_decode_make_plan(&p, &plan) == GQA_OK && plan.workspace_bytes > GQA_NOALLOC_SCRATCH_BYTES,
+        "a plan beyond the scratch array");
+  CHECK(gqa_decode_run_noalloc(&p, (void*)0x10000, (void*)0x10000, (void*)0x10000, (const int32_t*)0x10000, NULL,
+                               NULL, NULL, NULL, NULL, NULL, (void*)0x10000, (float*)0x10000, NULL) == GQA_ERR_WORKSPACE,
+        "no-allocation call beyond the scratch array refused");
+  p.s_q = 2;
+
   gqa_append_params ap;
   memset(&ap, 0, sizeof ap);
   ap.batch = 32;

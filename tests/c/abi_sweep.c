@@ -89,6 +89,16 @@ static void decode_case(const gqa_decode_params* p, long* ok_plans) {
   }
   st = gqa_resolve_rows(p, i32, i32, i32, i32, (int64_t*)FAKE, NULL);
   EXPECT(st == GQA_OK, "resolve failed after a good plan: %s", gqa_last_error());
+  /* the no-allocation entry point: the same plan, or a clear refusal when
+   * the partials exceed its scratch array */
+  const long long launches = gqa_stub_launches;
+  st = gqa_decode_run_noalloc(p, FAKE, FAKE, FAKE, i32, i32, i32, i32, f32, f32, FAKE, FAKE, (float*)FAKE, NULL);
+  if (plan.workspace_bytes > GQA_NOALLOC_SCRATCH_BYTES) {
+    EXPECT(st == GQA_ERR_WORKSPACE, "no-allocation call with %zu bytes of partials: status %d", plan.workspace_bytes, st);
+    EXPECT(gqa_stub_launches == launches, "a refused no-allocation call launched");
+  } else {
+    EXPECT(st == GQA_OK, "no-allocation call failed after a good plan: %s", gqa_last_error());
+  }
 }
 
 static void append_case(const gqa_append_params* p, long* ok_plans) {

@@ -65,6 +65,14 @@ hipError_t launch_resolve(const DecodeArgs&, int64_t* out, int list_cap, hipStre
   return hipSuccess;
 }
 
+// The no-allocation entry point's scratch array: a placeholder address
+// (16-byte aligned, never dereferenced on the host).
+hipError_t scratch_address(void** ptr, size_t* bytes) {
+  *ptr = reinterpret_cast<void*>(static_cast<uintptr_t>(0x7f0000000000ull));
+  *bytes = (size_t)32 << 20;
+  return hipSuccess;
+}
+
 hipError_t launch_append(const AppendArgs& a, hipStream_t) {
   need(a.chunk_tokens >= 1 && a.chunk_tokens <= kAppendMaxChunkTokens, "append chunk tokens");
   need((long long)a.chunk_tokens * a.h_kv * a.head_dim <= kAppendElemsPerWorkgroup || a.chunk_tokens == 1,
