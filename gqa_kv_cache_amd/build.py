@@ -3,7 +3,11 @@
     python -m gqa_kv_cache_amd.build          # or build() from Python
 
 Packed-fp32 instruction selection is disabled (-packed-fp32-ops off) for all
-device code.
+device code.  -fno-honor-nans: no NaN is ever produced on the path (masked
+scores are -inf, and every -inf - -inf is guarded), and NaN inputs are
+outside the contract, so every max need not quiet signalling NaNs first:
+without it each fmaxf became two canonicalising v_max plus the max itself
+(126 against 53 v_max in the 512-row kernel).
 """
 
 from __future__ import annotations
@@ -29,7 +33,7 @@ def hipcc() -> str:
 
 
 def command(out: str = LIB, extra=()):
-    return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared", "-fno-honor-nans",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-Wno-unused-command-line-argument",
             f"-I{INCLUDE}", f"-I{CSRC}", *extra,

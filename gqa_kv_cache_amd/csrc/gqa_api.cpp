@@ -379,6 +379,13 @@ void fill_args(gqa::DecodeArgs& a, const gqa_decode_params* p, const gqa_decode_
     a.part_ss = plan.rows;
   }
   combine_shape(p, plan, &a.comb_cols, &a.comb_rows);
+  // Row groups of a chunk on one XCD (see the partial kernel): only when
+  // the grid is a whole number of rounds of 8 x row groups.
+  {
+    const Tiling tl = plan_tiling(p, plan.rows, plan.math);
+    const int64_t wgs = plan.partial_workgroups;
+    a.xcd_rows = (tl.row_groups > 1 && wgs % ((int64_t)gqa::kXcds * tl.row_groups) == 0) ? tl.row_groups : 1;
+  }
   const float scale = p->softmax_scale != 0.f ? p->softmax_scale : 1.0f / std::sqrt((float)p->head_dim);
   a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
 }

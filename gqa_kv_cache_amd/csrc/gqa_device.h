@@ -93,8 +93,13 @@ struct DecodeArgs {
   int32_t heads_per_wg;       // KV heads one partial workgroup covers (1, 2 or 4)
   int32_t packed;             // 1: ragged cache split into equal row chunks (split s = chunk s)
   int32_t comb_cols, comb_rows;  // combine: column slices per row, rows per workgroup
+  int32_t xcd_rows;           // row groups whose workgroups share a chunk on one XCD (1: none)
   float scale_log2;           // softmax scale * log2(e)
 };
+
+// XCDs of MI355X; the dispatcher deals a grid's workgroups to them in turn
+// (workgroup i to XCD i mod 8).
+constexpr int kXcds = 8;
 
 // ---------------------------------------------------------------------------
 // Address policy.  A request's list has L entries: its n tokens (dense) or

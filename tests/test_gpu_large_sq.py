@@ -131,3 +131,18 @@ def test_large_sq_small_tiles_layouts(layout, kvd):
     s = spec(layout=layout, h_q=64, h_kv=4, s_q=8, head_dim=128, kv_dtype=kvd, gate=True, page_size=16,
              fixed_lengths=(333, 8, 1000, 0, 65))
     check_workload(gi.build(s, seed=1100), gate_mode="headwise", label=f"{kvd} {layout} 128 rows")
+
+
+# 512 rows per KV head in two row groups (d 128) or four (d 256) that share
+# their chunks on one XCD: every layout, and chunk sizes whose grids do and
+# do not divide into 8 x row groups (the planner falls back to the plain
+# workgroup order for the latter).
+XCD_CASES = [(gi.KV_BF16, 128, 0), (gi.KV_BF16, 128, 96), (gi.KV_FP8, 128, 0), (gi.KV_BF16, 256, 0)]
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "ragged", "paged"])
+@pytest.mark.parametrize("kvd,d,chunk", XCD_CASES)
+def test_row_groups_on_one_xcd(layout, kvd, d, chunk):
+    s = spec(layout=layout, h_q=64, h_kv=8, s_q=64, head_dim=d, kv_dtype=kvd, page_size=16,
+             gate=kvd != gi.KV_BF16, fixed_lengths=(600, 64, 250))
+    check_workload(gi.build(s, seed=1200 + d), kv_chunk=chunk, label=f"xcd row groups {layout} {kvd} d={d} chunk={chunk}")
