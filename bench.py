@@ -496,11 +496,15 @@ def bench_append(args):
     torch.cuda.synchronize()
     dev_us = statistics.mean(a.elapsed_time(b) for a, b in ev) * 1e3
     two_pass = wsb > 0
-    # bytes: bf16 K and V read, codes written, lengths and scales; the
-    # first-block policy over several workgroups reads the rows twice
+    # bytes: bf16 K and V read, codes written, lengths and scales.  The
+    # roofline counts the method's bytes only -- each row read once, each
+    # code written once -- although the first-block policy over several
+    # workgroups reads every row a second time (from the MALL when a
+    # request group fits it).
     pages_touched = B * (-(-S // P) + 1)
     min_bytes = elems * 2 * (2 + 1) + B * 4 * 2 + B * Hkv * 4 * 2 + pages_touched * 4
-    alg = elems * 2 * (2 + 1) + (elems * 2 * 2 if two_pass else 0)
+    alg = elems * 2 * (2 + 1)
+    launches = 2 if two_pass else 1
     us_per_call = wall / K * 1e6
     value = min_bytes / (us_per_call * 1e-6) / 1e9
     achieved = alg / (dev_us * 1e-6) / 1e9
@@ -522,13 +526,13 @@ def bench_append(args):
         "data": "synthetic",
         "config": {"workload": name, "batch": B, "new_tokens": S, "h_kv": Hkv, "head_dim": d, "kv_dtype": kvd,
                    "stored_tokens": int(w.seqlens[0]), "layout": "paged", "page_size": P,
-                   "scale_policy": policy, "seed": w.seed, "passes": 2 if two_pass else 1},
+                   "scale_policy": policy, "seed": w.seed, "launches": launches},
         "us_per_call": round(us_per_call, 3),
         "min_bytes_per_call": int(min_bytes),
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "roofline": {
             "bound": "hbm",
-            "kernel": "gqa_append_kernel" + (" (absmax pass + write pass)" if two_pass else ""),
+            "kernel": "gqa_append_kernel" + (" (maxima launch + write launch)" if two_pass else ""),
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",

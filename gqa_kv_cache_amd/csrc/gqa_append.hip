@@ -20,11 +20,9 @@
 // TB/s for a plain device-to-device copy of the same bytes.
 //
 // First-block scales: a request with n_b == 0 takes scale = absmax / 448
-// (FP8) or absmax / 127 (int8) per KV head over its appended rows.  One workgroup per request reduces its
-// rows in LDS; when a request's rows span several workgroups, a first pass
-// writes each workgroup's per-head maxima to the workspace and a
-// per-request pass reduces them to the scales (no atomics in HBM, no
-// zero-initialised memory).
+// (FP8) or absmax / 127 (int8) per KV head over its appended rows.  One
+// workgroup per request reduces its rows in LDS; requests whose rows span
+// several workgroups take a maxima launch first (see the kernel below).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -199,65 +197,63 @@ __device__ __forceinline__ int64_t append_row(const AppendArgs& a, int b, int64_
 
 }  // namespace
 
-// Three kernels, by PASS:
-//   0  per-workgroup absolute maxima of first-block requests whose rows span
-//      several workgroups, into the workspace;
-//   2  one workgroup per request: the maxima of all its workgroups -> its
-//      scales (written to k_scale / v_scale);
-//   1  the writes.  A first-block request covered by one workgroup takes its
-//      maxima in LDS here; every other request reads its scales.
-// Passes 0 and 2 run only when some first-block request spans several
-// workgroups.
-template <int PASS>
-__global__ void __launch_bounds__(kAppendThreads) gqa_append_kernel(AppendArgs a) {
+// Maxima of one workgroup's rows (c-th chunk of request b) into the
+// workspace: fp32 bits of |x|, K and V per head.
+__device__ __forceinline__ void chunk_maxima(const AppendArgs& a, int b, int c, uint32_t* smax) {
+  constexpr int U = 8;
+  const int t0 = c * a.chunk_tokens;
+  const int T = min(a.chunk_tokens, a.s_new - t0);
+  const int64_t in_base = ((int64_t)b * a.s_new + t0) * a.h_kv * a.head_dim;
+  for (int i = threadIdx.x; i < 2 * a.h_kv; i += kAppendThreads) smax[i] = 0u;
+  __syncthreads();
+  block_absmax<U>(a, in_base, T, smax);
+  __syncthreads();
+  for (int i = threadIdx.x; i < 2 * a.h_kv; i += kAppendThreads)
+    a.amax[((int64_t)b * a.chunks + c) * 2 * a.h_kv + i] = smax[i];
+}
+
+// The c-th chunk's writes of request b.  scales: 0 = the given ones (or none
+// for bf16), 1 = this workgroup's own maxima (the request fits one
+// workgroup), 2 = the request's per-workgroup maxima in the workspace.
+__device__ __forceinline__ void chunk_writes(const AppendArgs& a, int b, int c, int n, int scales, uint32_t* smax,
+                                             float* sscale, float* sinv, int64_t* srow) {
   constexpr int U = 8;  // 8-element items per thread in flight per round (K and V each)
-  __shared__ uint32_t smax[2 * kAppendMaxHeads];  // fp32 bits of |x| maxima (K, V per head)
-  __shared__ float sscale[2 * kAppendMaxHeads];
-  __shared__ float sinv[2 * kAppendMaxHeads];      // correctly rounded 1 / scale
-  __shared__ int64_t srow[kAppendMaxChunkTokens];  // physical row of each new token (-1: not written)
-  const int c = blockIdx.x, b = blockIdx.y;
-  const int n = a.seqlens[b];
-  const bool calib = a.fp8 && a.first_block && n == 0;
-  if (PASS != 1 && !calib) return;
   const int d8 = a.head_dim / 8;
   const int per_tok = a.h_kv * d8;  // 8-element items per token row
   const float qmax = a.int8 ? 127.f : 448.f;  // largest code magnitude
-
-  if (PASS == 2) {
-    // per-request reduction of the per-workgroup maxima
-    for (int i = threadIdx.x; i < 2 * a.h_kv; i += kAppendThreads) smax[i] = 0u;
-    __syncthreads();
-    const int total = a.chunks * 2 * a.h_kv;
-    for (int k = threadIdx.x; k < total; k += kAppendThreads)
-      atomicMax(&smax[k % (2 * a.h_kv)], a.amax[(int64_t)b * total + k]);
-    __syncthreads();
-    for (int i = threadIdx.x; i < 2 * a.h_kv; i += kAppendThreads) {
-      const float amax = __builtin_bit_cast(float, smax[i]);
-      ((i & 1) ? a.v_scale : a.k_scale)[(int64_t)b * a.h_kv + (i >> 1)] = amax > 0.f ? amax / qmax : 1.f;
-    }
-    return;
-  }
-
   const int t0 = c * a.chunk_tokens;
   const int T = min(a.chunk_tokens, a.s_new - t0);
   const int items = T * per_tok;
   const int64_t in_base = ((int64_t)b * a.s_new + t0) * a.h_kv * a.head_dim;
 
-  if (calib && (PASS == 0 || a.chunks == 1)) {
+  if (scales == 1) {
     for (int i = threadIdx.x; i < 2 * a.h_kv; i += kAppendThreads) smax[i] = 0u;
     __syncthreads();
     block_absmax<U>(a, in_base, T, smax);
+  } else if (scales == 2) {
+    // The request's per-workgroup maxima: each thread takes the running
+    // maximum of one (tensor, head) slot over every L-th workgroup in
+    // registers, then one LDS atomic (an atomic per value made all 256
+    // threads queue on the 2 H_kv slots).
+    for (int i = threadIdx.x; i < 2 * a.h_kv; i += kAppendThreads) smax[i] = 0u;
     __syncthreads();
-    if (PASS == 0) {
-      for (int i = threadIdx.x; i < 2 * a.h_kv; i += kAppendThreads)
-        a.amax[((int64_t)b * a.chunks + c) * 2 * a.h_kv + i] = smax[i];
-      return;
+    const int S2 = 2 * a.h_kv;
+    const int L = max(1, kAppendThreads / S2);
+    const uint32_t* am = a.amax + (int64_t)b * a.chunks * S2;
+    for (int idx = threadIdx.x; idx < S2 * L; idx += kAppendThreads) {
+      const int slot = idx % S2;
+      uint32_t m = 0u;
+      for (int cc = idx / S2; cc < a.chunks; cc += L) m = max(m, am[(int64_t)cc * S2 + slot]);
+      atomicMax(&smax[slot], m);
     }
+  }
+  __syncthreads();
+  if (scales != 0) {
     for (int i = threadIdx.x; i < 2 * a.h_kv; i += kAppendThreads) {
       const float amax = __builtin_bit_cast(float, smax[i]);
       const float s = amax > 0.f ? amax / qmax : 1.f;
       sscale[i] = s;
-      ((i & 1) ? a.v_scale : a.k_scale)[(int64_t)b * a.h_kv + (i >> 1)] = s;
+      if (c == 0) ((i & 1) ? a.v_scale : a.k_scale)[(int64_t)b * a.h_kv + (i >> 1)] = s;
     }
   } else if (a.fp8) {
     for (int i = threadIdx.x; i < 2 * a.h_kv; i += kAppendThreads)
@@ -310,17 +306,47 @@ __global__ void __launch_bounds__(kAppendThreads) gqa_append_kernel(AppendArgs a
   if (c == 0 && threadIdx.x == 0 && a.seqlens_out) a.seqlens_out[b] = n + a.s_new;
 }
 
-hipError_t launch_append(const AppendArgs& a, hipStream_t st) {
-  const dim3 grid(a.chunks, a.batch);
-  if (a.fp8 && a.first_block && a.chunks > 1) {
-    hipLaunchKernelGGL(gqa_append_kernel<0>, grid, dim3(kAppendThreads), 0, st, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(gqa_append_kernel<2>, dim3(1, a.batch), dim3(kAppendThreads), 0, st, a);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
+// One kernel for every append, in one of two roles: the maxima of a chunk
+// of a first-block request (into the workspace), or a chunk's writes.
+// Workgroup (c, y) takes chunk c of request y (maxima, or writes in request
+// order) or of request batch - 1 - y (writes after a maxima launch).
+// Without first-block requests spread over several workgroups one launch
+// writes everything.  With them, a first launch takes the maxima and a
+// second writes; each writing workgroup of such a request reduces the
+// request's per-workgroup maxima itself (no separate reduction launch), and
+// the writes take the requests last to first, so that the first re-read
+// rows are the ones the maxima launch read last, when the on-package cache
+// may still hold them.  No atomics in HBM, no zero-initialised memory.
+__global__ void __launch_bounds__(kAppendThreads) gqa_append_kernel(AppendArgs a) {
+  __shared__ uint32_t smax[2 * kAppendMaxHeads];  // fp32 bits of |x| maxima (K, V per head)
+  __shared__ float sscale[2 * kAppendMaxHeads];
+  __shared__ float sinv[2 * kAppendMaxHeads];      // correctly rounded 1 / scale
+  __shared__ int64_t srow[kAppendMaxChunkTokens];  // physical row of each new token (-1: not written)
+  const int c = blockIdx.x;
+  const int b = a.reverse ? a.batch - 1 - (int)blockIdx.y : (int)blockIdx.y;
+  const int n = a.seqlens[b];
+  const bool calib = a.fp8 && a.first_block && n == 0;
+  if (a.maxima) {
+    if (calib) chunk_maxima(a, b, c, smax);
+    return;
   }
-  hipLaunchKernelGGL(gqa_append_kernel<1>, grid, dim3(kAppendThreads), 0, st, a);
+  chunk_writes(a, b, c, n, calib ? (a.chunks == 1 ? 1 : 2) : 0, smax, sscale, sinv, srow);
+}
+
+hipError_t launch_append(const AppendArgs& a0, hipStream_t st) {
+  AppendArgs a = a0;
+  const dim3 grid(a.chunks, a.batch);
+  a.maxima = 0;
+  a.reverse = 0;
+  if (a.fp8 && a.first_block && a.chunks > 1) {
+    a.maxima = 1;
+    hipLaunchKernelGGL(gqa_append_kernel, grid, dim3(kAppendThreads), 0, st, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    a.maxima = 0;
+    a.reverse = 1;
+  }
+  hipLaunchKernelGGL(gqa_append_kernel, grid, dim3(kAppendThreads), 0, st, a);
   return hipGetLastError();
 }
 

@@ -31,6 +31,9 @@ struct AppendArgs {
   int32_t int8;
   int32_t seq_cap, page_shift, max_pages;
   int32_t chunk_tokens, chunks;
+  // Set by the launcher: 1 = this launch takes the maxima (else it
+  // writes); 1 = requests in reverse order.
+  int32_t maxima, reverse;
 };
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t st);
