@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -208,6 +209,18 @@ static_assert(gqa::kPWaves == 4, "row sharing is laid out for 4 waves per workgr
 Tiling plan_tiling(const gqa_decode_params* p, int rows, int math) {
   Tiling t;
   t.hpw = heads_per_wg(p->h_kv);
+  // Paged or top-K lists, up to 16 rows, H_kv a multiple of 8, and a wave
+  // that fits half the register file: one workgroup of eight waves covers
+  // eight KV heads, one each, and resolves the request's row table once for
+  // all of them.  MI355X, one process, partial kernel against two
+  // workgroups of four heads per CU: paged FP8 (32 x 32K, 64/8) 351 ->
+  // 329 us, sparse top-512 FP8 46.3 -> 45.1 us, int8 48.5 -> 48.1 us; dense
+  // lists were slower (FP8 64/8 at 128K 46.1 -> 51.0 us, bf16 d = 64 42.7 ->
+  // 46.1 us), so they keep four heads.
+  const bool indirect = p->layout == GQA_LAYOUT_PAGED || p->topk > 0;
+  if (math != GQA_MATH_VALU && rows <= 16 && indirect && p->h_kv % 8 == 0 &&
+      gqa::wide_fits(p->head_dim, one_byte(p)))
+    t.hpw = 8;
   if (math == GQA_MATH_VALU || rows <= 16) return t;
   if (rows <= 32) {
     if (p->head_dim == 256 && p->h_kv % 2 == 0) {
@@ -257,6 +270,7 @@ gqa_status make_plan(const gqa_decode_params* p, gqa_decode_plan* plan) {
   const int64_t L = p->topk > 0 ? p->topk : p->max_seqlen_kv;
   const int64_t pairs = (int64_t)p->batch * p->h_kv;
   const int hpw = tl.hpw;
+  const int lds_waves = hpw == 8 ? 8 : gqa::kPWaves;  // eight heads: a wave each
   // Resident workgroups per CU the grid is sized for.  Measured on MI355X
   // (one process, both plans): the row-sharing variants that fit two per CU
   // run faster with two (32 x 8192 tokens at S_q 16: 229 -> 202 us packed,
@@ -288,14 +302,14 @@ gqa_status make_plan(const gqa_decode_params* p, gqa_decode_plan* plan) {
       chunk = std::min<int64_t>(chunk, round_up(std::max<int64_t>(L, 1), 32));
       if (indirect) {
         // the row table (8 bytes per position) must fit beside the tiles
-        const size_t tiles = gqa::partial_lds_bytes(p->head_dim, one_byte(p), false, 0);
+        const size_t tiles = gqa::partial_lds_bytes(p->head_dim, one_byte(p), false, 0, lds_waves);
         chunk = std::min<int64_t>(chunk, (int64_t)((kMaxLdsPerWorkgroup - tiles) / 8 / 128 * 128));
       }
     }
   }
   // Shared memory of one partial workgroup (per-wave K/V tiles plus the
   // row table of paged / top-K chunks) must fit a workgroup's LDS.
-  const size_t lds = gqa::partial_lds_bytes(p->head_dim, one_byte(p), indirect, (int)chunk);
+  const size_t lds = gqa::partial_lds_bytes(p->head_dim, one_byte(p), indirect, (int)chunk, lds_waves);
   if (lds > kMaxLdsPerWorkgroup)
     return fail(GQA_ERR_UNSUPPORTED, "kv_chunk %lld needs %zu bytes of LDS per workgroup (limit %zu)",
                 (long long)chunk, lds, kMaxLdsPerWorkgroup);

@@ -51,6 +51,10 @@ __host__ __device__ constexpr int partial_wgs_per_cu(int D, bool fp8, int mb, in
              : 1;
 }
 constexpr int kPThreads = 64 * kPWaves;
+// The eight-wave, eight-head variant (one 16-row block per wave, the waves
+// splitting the tiles) exists where such a wave fits half the register
+// file: one-byte tiles at d <= 128 and bf16 tiles at d = 64.
+__host__ __device__ constexpr bool wide_fits(int D, bool fp8) { return (fp8 && D <= 128) || D == 64; }
 
 // Shared memory of the partial kernel: per wave a K tile (raw 16-byte
 // chunks) and a V tile (bf16), statically allocated; after the tile loop
@@ -60,10 +64,10 @@ __host__ __device__ constexpr int ktile_chunks(int D, bool fp8) { return kTile *
 __host__ __device__ constexpr int vtile_elems(int D) { return kTile * D; }
 __host__ __device__ constexpr int wave_tile_bytes(int D, bool fp8) { return ktile_chunks(D, fp8) * 16 + vtile_elems(D) * 2; }
 __host__ __device__ constexpr size_t table_bytes(bool indirect, int chunk) { return indirect ? (size_t)chunk * 8 : 0; }
-// LDS bytes of one partial workgroup: the tiles, the merge statistics and
-// the row table.
-__host__ __device__ constexpr size_t partial_lds_bytes(int D, bool fp8, bool indirect, int chunk) {
-  return (size_t)kPWaves * wave_tile_bytes(D, fp8) + 2 * kPWaves * 16 * 4 + table_bytes(indirect, chunk);
+// LDS bytes of one partial workgroup of `waves` waves: the tiles, the merge
+// statistics and the row table.
+__host__ __device__ constexpr size_t partial_lds_bytes(int D, bool fp8, bool indirect, int chunk, int waves = kPWaves) {
+  return (size_t)waves * wave_tile_bytes(D, fp8) + 2 * waves * 16 * 4 + table_bytes(indirect, chunk);
 }
 
 // Everything a kernel needs, passed by value (kernarg segment).
@@ -90,7 +94,7 @@ struct DecodeArgs {
   int32_t layout, causal, max_seqlen, seq_cap;
   int32_t page_shift, max_pages, topk_len, gate_mode;
   int32_t chunk, num_splits;
-  int32_t heads_per_wg;       // KV heads one partial workgroup covers (1, 2 or 4)
+  int32_t heads_per_wg;       // KV heads one partial workgroup covers (1, 2, 4 or 8)
   int32_t packed;             // 1: ragged cache split into equal row chunks (split s = chunk s)
   int32_t comb_cols, comb_rows;  // combine: column slices per row, rows per workgroup
   int32_t xcd_rows;           // row groups whose workgroups share a chunk on one XCD (1: none)

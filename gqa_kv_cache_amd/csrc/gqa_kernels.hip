@@ -106,14 +106,17 @@ constexpr int kDense = 0, kIndirect = 1, kPacked = 2;
 // sums far from overflow).
 constexpr float kLazyRescale = 8.f;
 
-// Waves of a partial workgroup: kPWaves, or eight for row sharing over
-// eight waves (two per SIMD in one workgroup).
-template <int SHARE>
-constexpr int partial_waves() { return SHARE == 8 ? 8 : kPWaves; }
+// Waves of a partial workgroup: kPWaves, or eight -- for row sharing over
+// eight waves, or (WIDE) for eight KV heads, one wave each -- two per SIMD
+// in one workgroup.
+template <int SHARE, bool WIDE = false>
+constexpr int partial_waves() { return SHARE == 8 || WIDE ? 8 : kPWaves; }
 
 // The launch bound's second value is waves per SIMD.
-template <int D, bool Q8, int MB, int RV, int SHARE>
-constexpr int partial_min_waves() { return partial_wgs_per_cu(D, Q8, MB, RV, SHARE) * partial_waves<SHARE>() / 4; }
+template <int D, bool Q8, int MB, int RV, int SHARE, bool WIDE = false>
+constexpr int partial_min_waves() {
+  return WIDE ? 2 : partial_wgs_per_cu(D, Q8, MB, RV, SHARE) * partial_waves<SHARE>() / 4;
+}
 
 // MB: 16-row MFMA blocks (RV = 0).  RV > 0 selects the VALU variant for up
 // to RV query rows (MB = 1): the same loads, LDS staging and pipeline, with
@@ -135,8 +138,15 @@ constexpr int partial_min_waves() { return partial_wgs_per_cu(D, Q8, MB, RV, SHA
 // row groups, each reading the chunk.  SHARE = 8 is a workgroup of eight
 // waves, two per SIMD, for one head: 128 or 256 rows read each tile once,
 // and while one wave of a SIMD runs its softmax the other's MFMAs run.
-template <int D, int KVT, int MODE, int MB, int RV, int SHARE>
-__global__ void __launch_bounds__(64 * partial_waves<SHARE>(), (partial_min_waves<D, KVT != kKvBf16, MB, RV, SHARE>()))
+// WIDE: a workgroup of eight waves, one per KV head (HPW = 8), for the
+// one-block variants whose registers fit two waves per SIMD (one-byte tiles
+// at d <= 128, bf16 at d = 64).  A CU then runs one workgroup whose eight
+// waves stream alike, where two four-wave workgroups per CU stream unequally
+// (the older one's waves win the CU's issue arbitration); a top-K or paged
+// request's row table is resolved once for all eight heads.
+template <int D, int KVT, int MODE, int MB, int RV, int SHARE, bool WIDE = false>
+__global__ void __launch_bounds__((64 * partial_waves<SHARE, WIDE>()),
+                                  (partial_min_waves<D, KVT != kKvBf16, MB, RV, SHARE, WIDE>()))
     gqa_partial_kernel(DecodeArgs a) {
   constexpr bool Q8 = KVT != kKvBf16;          // one-byte codes (FP8 or int8) with scales
   using TS = TileShape<D, Q8>;
@@ -152,11 +162,12 @@ __global__ void __launch_bounds__(64 * partial_waves<SHARE>(), (partial_min_wave
   static_assert(SHARE == 1 || ((SHARE == 2 || SHARE == 4 || SHARE == 8) && RV == 0 && MB <= 2 &&
                                 (NLD % SHARE == 0 || SHARE % NLD == 0)),
                 "row sharing: 2, 4 or 8 waves per head, one or two blocks per wave");
-  constexpr int NW = partial_waves<SHARE>();    // waves of this workgroup
+  static_assert(!WIDE || (SHARE == 1 && RV == 0 && MB == 1), "eight heads: one block, waves split the tiles");
+  constexpr int NW = partial_waves<SHARE, WIDE>();  // waves of this workgroup
   constexpr int NT = 64 * NW;
   // LDS tiles: one per wave, or two per head (row sharing; eight waves
   // cover one head)
-  constexpr int NTILE = SHARE == 8 ? 2 : kPWaves;
+  constexpr int NTILE = SHARE == 8 ? 2 : (SHARED ? kPWaves : NW);
   constexpr bool INDIRECT = MODE == kIndirect;
   constexpr bool PACKED = MODE == kPacked;
   constexpr bool VALU = RV > 0;
@@ -167,7 +178,7 @@ __global__ void __launch_bounds__(64 * partial_waves<SHARE>(), (partial_min_wave
   // through LDS after the tile loop: four floats of padding put the 16 rows
   // one store covers on different banks.
   constexpr int WST = D + 4;
-  static_assert(kPWaves * 16 * WST * 4 <= kPWaves * wave_tile_bytes(D, Q8), "accumulators fit in the tiles");
+  static_assert(SHARED || NW * 16 * WST * 4 <= NTILE * wave_tile_bytes(D, Q8), "accumulators fit in the tiles");
   // Lazy rescaling (below) keeps a tile's scores live across a branch; the
   // variants with the most accumulators (four blocks, or two of d = 256)
   // would spill for it, and rescale at every tile instead.
@@ -175,7 +186,7 @@ __global__ void __launch_bounds__(64 * partial_waves<SHARE>(), (partial_min_wave
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __shared__ __attribute__((aligned(16))) unsigned char tiles[NTILE * wave_tile_bytes(D, Q8)];
-  __shared__ float wstat[2 * kPWaves * 16];
+  __shared__ float wstat[2 * NW * 16];
 
   const int lane = threadIdx.x & 63;
   // Wave index as a scalar: tile-level control flow is then uniform, which
@@ -921,7 +932,7 @@ __global__ void __launch_bounds__(64 * partial_waves<SHARE>(), (partial_min_wave
     // Merge the waves of each head, one 16-row block at a time, and write.
     float* wacc = reinterpret_cast<float*>(tiles);
     float* wm = wstat;
-    float* wl = wstat + kPWaves * 16;
+    float* wl = wstat + NW * 16;
     const bool final_out = fin;
     constexpr int D8 = D / 8;
 #pragma unroll
@@ -956,7 +967,7 @@ __global__ void __launch_bounds__(64 * partial_waves<SHARE>(), (partial_min_wave
       __syncthreads();
 
       const int nrow = min(16, a.rows - mb * 16);
-      for (int it = threadIdx.x; it < hpw * nrow * D8; it += kPThreads) {
+      for (int it = threadIdx.x; it < hpw * nrow * D8; it += NT) {
         const int hh = it / (nrow * D8);
         const int rem = it - hh * (nrow * D8);
         const int rl = rem / D8;
@@ -1186,18 +1197,19 @@ __global__ void __launch_bounds__(kThreads) gqa_resolve_kernel(DecodeArgs a, int
 
 // ev0 / ev1 (may be null): events stamped by the dispatch itself at the
 // kernel's start and end, so they time the kernel alone.
-template <int D, int KVT, int MODE, int MB, int RV, int SHARE = 1>
+template <int D, int KVT, int MODE, int MB, int RV, int SHARE = 1, bool WIDE = false>
 static hipError_t launch_partial_t(const DecodeArgs& a, dim3 grid, hipStream_t st, hipEvent_t ev0,
                                    hipEvent_t ev1) {
   const size_t lds = table_bytes(MODE == kIndirect, a.chunk);
-  hipExtLaunchKernelGGL((gqa_partial_kernel<D, KVT, MODE, MB, RV, SHARE>), grid, dim3(64 * partial_waves<SHARE>()),
-                        lds, st, ev0, ev1, 0, a);
+  hipExtLaunchKernelGGL((gqa_partial_kernel<D, KVT, MODE, MB, RV, SHARE, WIDE>), grid,
+                        dim3(64 * partial_waves<SHARE, WIDE>()), lds, st, ev0, ev1, 0, a);
   return hipGetLastError();
 }
 
 // rv > 0: the VALU variant for up to rv rows (1, 2, 4 or 8); share = 2, 4
 // or 8: that many waves per head split the rows, mb 16-row blocks each;
-// else mb MFMA blocks per wave, the waves of a head splitting the tiles.
+// else mb MFMA blocks per wave, the waves of a head splitting the tiles
+// (eight waves for eight heads when a.heads_per_wg is 8).
 template <int D, int KVT, int MODE>
 static hipError_t launch_mb(const DecodeArgs& a, int mb, int rv, int share, dim3 grid, hipStream_t st,
                             hipEvent_t ev0, hipEvent_t ev1) {
@@ -1219,6 +1231,11 @@ static hipError_t launch_mb(const DecodeArgs& a, int mb, int rv, int share, dim3
   if (share == 8) {
     if (mb == 1) return launch_partial_t<D, KVT, MODE, 1, 0, 8>(a, grid, st, ev0, ev1);
     if constexpr (D <= 128) return launch_partial_t<D, KVT, MODE, 2, 0, 8>(a, grid, st, ev0, ev1);
+    return hipErrorInvalidValue;
+  }
+  if (a.heads_per_wg == 8) {
+    if constexpr (wide_fits(D, KVT != kKvBf16))
+      if (mb == 1 && rv == 0) return launch_partial_t<D, KVT, MODE, 1, 0, 1, true>(a, grid, st, ev0, ev1);
     return hipErrorInvalidValue;
   }
   if constexpr (D <= 128) {
