@@ -166,12 +166,14 @@ unsigned __int128 partial_o_bytes(const gqa_decode_params* p, const gqa_decode_p
 
 unsigned __int128 round_up_256(unsigned __int128 x) { return (x + 255) / 256 * 256; }
 
-// The math path GQA_MATH_AUTO takes for a group of `rows` query rows.
-// Measured on MI355X over 128K-token decodes (bf16 d = 128 and 64, FP8
-// d = 128; three processes each): MFMA is 5-7 % faster from 2 rows up and
-// more than twice as fast at 8, its time flat from 1 to 16 rows; at 1 row
-// the VALU path is as fast or up to 1 % faster.
-int auto_math(int rows, int head_dim) { return rows == 1 && head_dim <= 128 ? GQA_MATH_VALU : GQA_MATH_MFMA; }
+// The math path GQA_MATH_AUTO takes for a group of `rows` query rows: the
+// matrix units at every row count.  Measured on MI355X over 128K-token
+// decodes at H_kv = 8 (bf16 d = 128 and 64, FP8 and int8 d = 128; three
+// processes each): MFMA is faster from 2 rows up (more than twice as fast
+// at 8), its time flat from 1 to 16 rows; at 1 row it is as fast or faster
+// too (partial kernel, bf16 d = 128: 81.1-81.8 against 83.1-83.5 us; d = 64:
+// 42.2-42.4 against 42.5-43.1; int8: 44.5-46.0 against 49.6-51.1; FP8 equal).
+int auto_math(int, int) { return GQA_MATH_MFMA; }
 
 // How a KV head's query rows are laid over waves and workgroups.
 struct Tiling {

@@ -88,7 +88,8 @@ enum { GQA_GATE_NONE = 0, GQA_GATE_ELEMENTWISE = 1, GQA_GATE_HEADWISE = 2 };
  *   GQA_MATH_VALU  v_dot2_f32_bf16 and fp32 FMAs on exactly the group's rows,
  *                  for at most 8 query rows per KV head;
  *   GQA_MATH_AUTO  the faster one for the row count, as measured on MI355X:
- *                  VALU for 1 row, MFMA from 2 rows up.
+ *                  MFMA at every row count (VALU is at best level with it
+ *                  at 1 row and slower from 2 rows up).
  * At decode the products are skinny (rows = (H_q / H_kv) * S_q by d); a
  * tile sized for prefill leaves almost every row of a matrix-unit tile idle
  * ("When the K/V copy costs more than the attention", "What I was looking

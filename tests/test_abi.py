@@ -118,8 +118,8 @@ def test_plan_math_paths():
     assert plan["math"] == 1 and plan["row_blocks"] == 1
     plan = G.gqa_decode_make_plan(base(math="auto", h_q=64, h_kv=2))   # 32 rows: MFMA only
     assert plan["math"] == 1 and plan["row_blocks"] == 2
-    # the measured crossover: VALU for one row per KV head, MFMA from two
-    assert G.gqa_decode_make_plan(base(math="auto", h_q=8, h_kv=8))["math"] == 2
+    # the measured choice: MFMA at every row count (VALU only when asked for)
+    assert G.gqa_decode_make_plan(base(math="auto", h_q=8, h_kv=8))["math"] == 1
     assert G.gqa_decode_make_plan(base(math="auto", h_q=8, h_kv=4))["math"] == 1
 
 
