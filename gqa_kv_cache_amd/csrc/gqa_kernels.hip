@@ -2,9 +2,10 @@
 //
 // Split-KV partial kernel.  A workgroup of 4 wave64s covers one list chunk
 // of one request for HPW consecutive KV heads (HPW = 4 when H_kv allows,
-// else 2 or 1).  Wave w works on head g0 + w % HPW; the 4 / HPW waves that
-// share a head take alternate 32-position tiles of the chunk and are merged
-// in LDS at the end.  With HPW = 4 the workgroup reads, for every token, a
+// else 2 or 1; paged and top-K lists can take eight, one wave each, in a
+// workgroup of 8 wave64s -- WIDE below).  Wave w works on head g0 + w % HPW;
+// the waves that share a head take alternate 32-position tiles of the chunk
+// and are merged in LDS at the end.  With HPW = 4 the workgroup reads, for every token, a
 // contiguous 1 KiB of the cache (four heads' K or V), which is what lets
 // HBM run close to its streaming rate.  Groups of more than 16 query rows
 // per KV head can instead split the rows over the waves of a head (two,
@@ -206,7 +207,7 @@ __global__ void __launch_bounds__((64 * partial_waves<SHARE, WIDE>()),
   // (L / 8) mod R and unit ((L / 8) / R) * 8 + L mod 8 of the units
   // (split, head group, request); the host sets R (xcd_rows) only when the
   // grid divides into 8 R.  On MI355X, 64 query tokens of 64/8 heads over
-  // 128K tokens (two row groups): FETCH 2.02 -> 1.02 times the K/V bytes,
+  // 128K tokens (two row groups): FETCH 2.02 -> 1.04 times the K/V bytes,
   // 333.5 -> 304.6 us.
   unsigned bx = blockIdx.x, by = blockIdx.y, bz = blockIdx.z;
   if (a.xcd_rows > 1) {
