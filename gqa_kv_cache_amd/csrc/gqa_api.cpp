@@ -225,11 +225,19 @@ Tiling plan_tiling(const gqa_decode_params* p, int rows, int math) {
     t.hpw = 8;
   if (math == GQA_MATH_VALU || rows <= 16) return t;
   if (rows <= 32) {
-    if (p->head_dim == 256 && p->h_kv % 2 == 0) {
+    if (p->head_dim == 256 && !one_byte(p) && !packed_mode(p)) {
+      // bf16 d = 256: two blocks per wave with Q in LDS, one KV head per
+      // workgroup (the Q buffer holds one head).  MI355X, 32/2 heads at 128K,
+      // against the two waves per head sharing tiles: partial kernel
+      // 55.7 -> 54.5 us, call 60.7 -> 58.4 us (half the splits).  FP8 ran
+      // slower this way (40.4 against 35.5 us) and keeps the shared tiles.
+      t.mb = 2;
+      t.hpw = 1;
+    } else if (p->head_dim == 256 && p->h_kv % 2 == 0) {
       t.share = 2;
       t.hpw = 2;
     } else {
-      t.mb = 2;
+      t.mb = 2;  // odd H_kv: one head per workgroup (bf16 d = 256 keeps Q in LDS)
     }
     return t;
   }
@@ -273,6 +281,9 @@ gqa_status make_plan(const gqa_decode_params* p, gqa_decode_plan* plan) {
   const int64_t pairs = (int64_t)p->batch * p->h_kv;
   const int hpw = tl.hpw;
   const int lds_waves = hpw == 8 ? 8 : gqa::kPWaves;  // eight heads: a wave each
+  const size_t q_bytes = gqa::q_in_lds(p->head_dim, one_byte(p), tl.mb, plan->math == GQA_MATH_VALU ? 1 : 0, tl.share)
+                             ? gqa::q_lds_bytes(p->head_dim, tl.mb)
+                             : 0;
   // Resident workgroups per CU the grid is sized for.  Measured on MI355X
   // (one process, both plans): the row-sharing variants that fit two per CU
   // run faster with two (32 x 8192 tokens at S_q 16: 229 -> 202 us packed,
@@ -304,14 +315,14 @@ gqa_status make_plan(const gqa_decode_params* p, gqa_decode_plan* plan) {
       chunk = std::min<int64_t>(chunk, round_up(std::max<int64_t>(L, 1), 32));
       if (indirect) {
         // the row table (8 bytes per position) must fit beside the tiles
-        const size_t tiles = gqa::partial_lds_bytes(p->head_dim, one_byte(p), false, 0, lds_waves);
+        const size_t tiles = gqa::partial_lds_bytes(p->head_dim, one_byte(p), false, 0, lds_waves, q_bytes);
         chunk = std::min<int64_t>(chunk, (int64_t)((kMaxLdsPerWorkgroup - tiles) / 8 / 128 * 128));
       }
     }
   }
   // Shared memory of one partial workgroup (per-wave K/V tiles plus the
   // row table of paged / top-K chunks) must fit a workgroup's LDS.
-  const size_t lds = gqa::partial_lds_bytes(p->head_dim, one_byte(p), indirect, (int)chunk, lds_waves);
+  const size_t lds = gqa::partial_lds_bytes(p->head_dim, one_byte(p), indirect, (int)chunk, lds_waves, q_bytes);
   if (lds > kMaxLdsPerWorkgroup)
     return fail(GQA_ERR_UNSUPPORTED, "kv_chunk %lld needs %zu bytes of LDS per workgroup (limit %zu)",
                 (long long)chunk, lds, kMaxLdsPerWorkgroup);

@@ -55,6 +55,12 @@ constexpr int kPThreads = 64 * kPWaves;
 // splitting the tiles) exists where such a wave fits half the register
 // file: one-byte tiles at d <= 128 and bf16 tiles at d = 64.
 __host__ __device__ constexpr bool wide_fits(int D, bool fp8) { return (fp8 && D <= 128) || D == 64; }
+// Two 16-row MFMA blocks of bf16 d = 256 per wave (the waves splitting the
+// tiles) keep Q's operands in LDS, 16 KiB for the workgroup's one KV head.
+__host__ __device__ constexpr bool q_in_lds(int D, bool fp8, int mb, int rv, int share) {
+  return D == 256 && !fp8 && mb == 2 && rv == 0 && share == 1;
+}
+__host__ __device__ constexpr size_t q_lds_bytes(int D, int mb) { return (size_t)mb * (D / 32) * 64 * 16; }
 
 // Shared memory of the partial kernel: per wave a K tile (raw 16-byte
 // chunks) and a V tile (bf16), statically allocated; after the tile loop
@@ -65,9 +71,10 @@ __host__ __device__ constexpr int vtile_elems(int D) { return kTile * D; }
 __host__ __device__ constexpr int wave_tile_bytes(int D, bool fp8) { return ktile_chunks(D, fp8) * 16 + vtile_elems(D) * 2; }
 __host__ __device__ constexpr size_t table_bytes(bool indirect, int chunk) { return indirect ? (size_t)chunk * 8 : 0; }
 // LDS bytes of one partial workgroup of `waves` waves: the tiles, the merge
-// statistics and the row table.
-__host__ __device__ constexpr size_t partial_lds_bytes(int D, bool fp8, bool indirect, int chunk, int waves = kPWaves) {
-  return (size_t)waves * wave_tile_bytes(D, fp8) + 2 * waves * 16 * 4 + table_bytes(indirect, chunk);
+// statistics, Q (when it is kept in LDS, `q_bytes`) and the row table.
+__host__ __device__ constexpr size_t partial_lds_bytes(int D, bool fp8, bool indirect, int chunk, int waves = kPWaves,
+                                                       size_t q_bytes = 0) {
+  return (size_t)waves * wave_tile_bytes(D, fp8) + 2 * waves * 16 * 4 + q_bytes + table_bytes(indirect, chunk);
 }
 
 // Everything a kernel needs, passed by value (kernarg segment).

@@ -184,10 +184,15 @@ __global__ void __launch_bounds__((64 * partial_waves<SHARE, WIDE>()),
   // variants with the most accumulators (four blocks, or two of d = 256)
   // would spill for it, and rescale at every tile instead.
   constexpr bool LAZY = MB * D <= 256;
+  // Two 16-row blocks of bf16 d = 256 per wave keep Q in LDS (the host plans
+  // them with one KV head per workgroup): Q's 64 VGPRs of MFMA operands would
+  // otherwise spill the wave's registers.
+  constexpr bool QLDS = q_in_lds(D, KVT != kKvBf16, MB, RV, SHARE) && !WIDE;
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __shared__ __attribute__((aligned(16))) unsigned char tiles[NTILE * wave_tile_bytes(D, Q8)];
   __shared__ float wstat[2 * NW * 16];
+  __shared__ u32x4 qbuf[QLDS ? MB * KK * 64 : 1];  // Q operands, lane-major (QLDS)
 
   const int lane = threadIdx.x & 63;
   // Wave index as a scalar: tile-level control flow is then uniform, which
@@ -372,6 +377,19 @@ __global__ void __launch_bounds__((64 * partial_waves<SHARE, WIDE>()),
     }
     sc = fmaxf(sc, 1.17549435e-38f);
   }
+  if constexpr (QLDS) {
+    // Lane `lane` of k-step kk of block mb reads its B operand from
+    // qbuf[(mb * KK + kk) * 64 + lane]: 16 consecutive bytes per lane, no
+    // bank conflicts.  One wave of the head writes it (the other waves hold
+    // the same values).
+    if (sub == 0) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) qbuf[(mb * KK + kk) * 64 + lane] = qop[mb][kk];
+    }
+    __syncthreads();
+  }
 
   f32x4 acc[VALU ? 1 : MB][NB];
   float accv[VALU ? RV : 1][ELT];
@@ -498,7 +516,12 @@ __global__ void __launch_bounds__((64 * partial_waves<SHARE, WIDE>()),
       for (int mb = 0; mb < MB; ++mb) {
         f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) c = mfma_16x16x32(kop[kk], qop[mb][kk], c);
+        for (int kk = 0; kk < KK; ++kk) {
+          if constexpr (QLDS)
+            c = mfma_16x16x32(kop[kk], qbuf[(mb * KK + kk) * 64 + lane], c);
+          else
+            c = mfma_16x16x32(kop[kk], qop[mb][kk], c);
+        }
         s[hb][mb] = LAZY ? c : c * sc;        // LAZY: unscaled, sc > 0 is applied in the exponent
       }
       if constexpr (D == 256) __builtin_amdgcn_sched_barrier(0);
@@ -1234,6 +1257,8 @@ static hipError_t launch_mb(const DecodeArgs& a, int mb, int rv, int share, dim3
     if constexpr (D <= 128) return launch_partial_t<D, KVT, MODE, 2, 0, 8>(a, grid, st, ev0, ev1);
     return hipErrorInvalidValue;
   }
+  // Q kept in LDS holds one KV head.
+  if (q_in_lds(D, KVT != kKvBf16, mb, rv, share) && a.heads_per_wg != 1) return hipErrorInvalidValue;
   if (a.heads_per_wg == 8) {
     if constexpr (wide_fits(D, KVT != kKvBf16))
       if (mb == 1 && rv == 0) return launch_partial_t<D, KVT, MODE, 1, 0, 1, true>(a, grid, st, ev0, ev1);

@@ -45,7 +45,10 @@ hipError_t launch_partial(const DecodeArgs& a, int D, int kvt, int mode, int mb,
   need(a.heads_per_wg != 8 || (share == 1 && mb == 1 && rv == 0 && wide_fits(D, kvt != kKvBf16)),
        "eight heads per workgroup only for the one-block variants that fit two waves per SIMD");
   const int waves = a.heads_per_wg == 8 ? 8 : kPWaves;
-  need(partial_lds_bytes(D, kvt != kKvBf16, mode == 1, a.chunk, waves) <= 160 * 1024, "LDS per workgroup");
+  const bool qlds = q_in_lds(D, kvt != kKvBf16, mb, rv, share);
+  need(!qlds || a.heads_per_wg == 1, "Q kept in LDS holds one KV head");
+  need(partial_lds_bytes(D, kvt != kKvBf16, mode == 1, a.chunk, waves, qlds ? q_lds_bytes(D, mb) : 0) <= 160 * 1024,
+       "LDS per workgroup");
   need(a.q && a.k && a.v && a.o && a.lse, "required pointers");
   need(mode != 1 || a.block_table || a.topk, "indirect mode without a table");
   need(a.num_splits == 1 && !a.packed ? true : (a.o_part && a.lse_part), "partials without a workspace");
