@@ -185,9 +185,11 @@ struct Tiling {
 static_assert(gqa::kPWaves == 4, "row sharing is laid out for 4 waves per workgroup");
 
 // Up to 16 rows: one block per wave, the waves of a head taking alternate
-// tiles.  17-32 rows: two blocks per wave, except d = 256 (two blocks of
-// d = 256 do not fit a wave's registers), where a head's two waves split
-// the rows and share the tiles through LDS (even H_kv).  Eight waves per
+// tiles.  17-32 rows: two blocks per wave.  At d = 256 two blocks fit a
+// wave's registers only with Q moved to LDS, which the bf16 kernels do
+// (contiguous, paged and top-K lists); one-byte codes and packed caches
+// with an even H_kv instead have a head's two waves split the rows and
+// share the tiles through LDS.  Eight waves per
 // head there (two with rows, all eight loading) ran the partial kernel
 // faster for bf16 (54.3 against 55.8 us, 32/2 heads at 128K) but the whole
 // call slower in back-to-back calls (64.7 against 63.3 us), and FP8 slower
