@@ -318,7 +318,8 @@ gqa_status make_plan(const gqa_decode_params* p, gqa_decode_plan* plan) {
       if (indirect) {
         // the row table (8 bytes per position) must fit beside the tiles
         const size_t tiles = gqa::partial_lds_bytes(p->head_dim, one_byte(p), false, 0, lds_waves, q_bytes);
-        chunk = std::min<int64_t>(chunk, (int64_t)((kMaxLdsPerWorkgroup - tiles) / 8 / 128 * 128));
+        chunk = std::min<int64_t>(chunk, (int64_t)((kMaxLdsPerWorkgroup - tiles - gqa::table_bytes(true, 0)) / 8 /
+                                                   128 * 128));
       }
     }
   }

@@ -69,7 +69,12 @@ __host__ __device__ constexpr size_t q_lds_bytes(int D, int mb) { return (size_t
 __host__ __device__ constexpr int ktile_chunks(int D, bool fp8) { return kTile * D * (fp8 ? 1 : 2) / 16; }
 __host__ __device__ constexpr int vtile_elems(int D) { return kTile * D; }
 __host__ __device__ constexpr int wave_tile_bytes(int D, bool fp8) { return ktile_chunks(D, fp8) * 16 + vtile_elems(D) * 2; }
-__host__ __device__ constexpr size_t table_bytes(bool indirect, int chunk) { return indirect ? (size_t)chunk * 8 : 0; }
+// Paged top-K lists also copy the request's block-table row, when it has at
+// most kBtCache pages, to LDS beside the row table (4 KiB).
+constexpr int kBtCache = 1024;
+__host__ __device__ constexpr size_t table_bytes(bool indirect, int chunk) {
+  return indirect ? (size_t)chunk * 8 + (size_t)kBtCache * 4 : 0;
+}
 // LDS bytes of one partial workgroup of `waves` waves: the tiles, the merge
 // statistics, Q (when it is kept in LDS, `q_bytes`) and the row table.
 __host__ __device__ constexpr size_t partial_lds_bytes(int D, bool fp8, bool indirect, int chunk, int waves = kPWaves,

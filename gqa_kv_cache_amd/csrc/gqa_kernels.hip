@@ -272,16 +272,32 @@ __global__ void __launch_bounds__((64 * partial_waves<SHARE, WIDE>()),
   // the end are masked).  The loads are ordered for their in-order return:
   // a thread's top-K entries first, then Q, the scales and the gate (which
   // do not depend on the table), then the block-table entries, so that each
-  // wait covers only loads issued before what it waits for.
+  // wait covers only loads issued before what it waits for.  A paged top-K
+  // list whose request has at most kBtCache pages loads the request's whole
+  // block-table row next to its top-K entries (the two do not depend on each
+  // other) and looks pages up in LDS: one dependent HBM round trip fewer
+  // before the first tile's loads.
   int32_t* trow = reinterpret_cast<int32_t*>(smem);
   int32_t* ttok = trow + a.chunk;
+  int32_t* btc = ttok + a.chunk;                  // the block-table row (paged top-K lists)
   constexpr int RPT = INDIRECT ? 4096 / NT : 1;   // slots per thread at the largest chunk
+  constexpr int BTR = INDIRECT ? kBtCache / NT : 1;
   int tk[RPT];
+  int btv[BTR];
+  int npg = 0;
+  bool btc_on = false;
   if constexpr (INDIRECT) {
 #pragma unroll
     for (int k = 0; k < RPT; ++k) {
       const int p = threadIdx.x + k * NT;
       tk[k] = (p < a.chunk && start + p < end) ? slot_token(a, b, n, start + p) : -1;
+    }
+    npg = (n + (1 << a.page_shift) - 1) >> a.page_shift;
+    btc_on = a.layout == kLayoutPaged && a.topk_len > 0 && npg <= kBtCache;
+#pragma unroll
+    for (int k = 0; k < BTR; ++k) {
+      const int p = threadIdx.x + k * NT;
+      btv[k] = (btc_on && p < npg) ? a.block_table[(int64_t)b * a.max_pages + p] : 0;
     }
     __asm__ __volatile__("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
@@ -352,11 +368,29 @@ __global__ void __launch_bounds__((64 * partial_waves<SHARE, WIDE>()),
   if constexpr (INDIRECT) {
     __asm__ __volatile__("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
+    if (btc_on) {
+#pragma unroll
+      for (int k = 0; k < BTR; ++k) {
+        const int p = threadIdx.x + k * NT;
+        if (p < npg) btc[p] = btv[k];
+      }
+      __syncthreads();
+    }
 #pragma unroll
     for (int k = 0; k < RPT; ++k) {
       const int p = threadIdx.x + k * NT;
       if (p < a.chunk) {
-        trow[p] = tk[k] >= 0 ? (int32_t)token_row(a, b, tk[k], base) : 0;
+        int32_t row = 0;
+        if (tk[k] >= 0) {
+          if (btc_on) {
+            const int64_t r = ((int64_t)btc[tk[k] >> a.page_shift] << a.page_shift) +
+                              (tk[k] & ((1 << a.page_shift) - 1));
+            row = (int32_t)min(max(r, (int64_t)0), a.kv_rows - 1);
+          } else {
+            row = (int32_t)token_row(a, b, tk[k], base);
+          }
+        }
+        trow[p] = row;
         ttok[p] = tk[k];
       }
     }
