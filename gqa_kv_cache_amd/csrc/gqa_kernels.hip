@@ -292,8 +292,9 @@ __global__ void __launch_bounds__((64 * partial_waves<SHARE, WIDE>()),
       const int p = threadIdx.x + k * NT;
       tk[k] = (p < a.chunk && start + p < end) ? slot_token(a, b, n, start + p) : -1;
     }
-    npg = (n + (1 << a.page_shift) - 1) >> a.page_shift;
-    btc_on = a.layout == kLayoutPaged && a.topk_len > 0 && npg <= kBtCache;
+    const int64_t pages = ((int64_t)n + (1 << a.page_shift) - 1) >> a.page_shift;  // no int overflow near 2^31
+    btc_on = a.layout == kLayoutPaged && a.topk_len > 0 && pages <= kBtCache;
+    npg = btc_on ? (int)pages : 0;
 #pragma unroll
     for (int k = 0; k < BTR; ++k) {
       const int p = threadIdx.x + k * NT;
