@@ -134,6 +134,43 @@ def test_plan_head_dim_256():
     assert plan["kv_chunk"] <= 4032
 
 
+def test_plan_heads_per_workgroup():
+    # Paged and top-K lists with H_kv a multiple of 8 and one-byte K/V at d 128 (at most 16
+    # rows): one workgroup covers all eight KV heads, so the grid holds one head group.
+    kw = dict(batch=4, h_q=32, h_kv=8, kv_dtype="fp8_e4m3fn", max_seqlen_kv=512, seq_capacity=512, kv_rows=4 * 512)
+    for extra in (dict(layout="paged", page_size=16, max_pages_per_seq=32), dict(topk=128)):
+        plan = G.gqa_decode_make_plan(base(**kw, **extra))
+        assert plan["partial_workgroups"] == plan["num_splits"] * 1 * 4, (extra, plan)
+    # the same shape as a dense list, and bf16 d = 128 paged (two waves per SIMD do not
+    # fit), keep four heads per workgroup: two head groups
+    plan = G.gqa_decode_make_plan(base(**kw))
+    assert plan["partial_workgroups"] == plan["num_splits"] * 2 * 4, plan
+    plan = G.gqa_decode_make_plan(base(**dict(kw, kv_dtype="bf16"), layout="paged", page_size=16,
+                                       max_pages_per_seq=32))
+    assert plan["partial_workgroups"] == plan["num_splits"] * 2 * 4, plan
+    # more than 16 rows: four heads
+    plan = G.gqa_decode_make_plan(base(**dict(kw, h_q=256), layout="paged", page_size=16, max_pages_per_seq=32))
+    assert plan["partial_workgroups"] % (plan["num_splits"] * 4) == 0 and plan["rows"] == 32
+
+
+def test_plan_d256_two_row_blocks():
+    # 32 rows at d 256: bf16 keeps Q in LDS with one KV head per workgroup (two head
+    # groups for H_kv 2); FP8 has a head's two waves share the tiles, two heads per workgroup
+    kw = dict(head_dim=256, h_q=32, h_kv=2, s_q=2, batch=1, max_seqlen_kv=131072, seq_capacity=131072,
+              kv_rows=131072)
+    plan = G.gqa_decode_make_plan(base(**kw, kv_dtype="bf16"))
+    assert plan["row_blocks"] == 2 and plan["partial_workgroups"] == plan["num_splits"] * 2, plan
+    plan = G.gqa_decode_make_plan(base(**kw, kv_dtype="fp8_e4m3fn"))
+    assert plan["row_blocks"] == 2 and plan["partial_workgroups"] == plan["num_splits"] * 1, plan
+    # a packed ragged bf16 cache keeps the shared tiles too
+    plan = G.gqa_decode_make_plan(base(**dict(kw, seq_capacity=0), kv_dtype="bf16", layout="ragged"))
+    assert plan["row_blocks"] == 2 and plan["partial_workgroups"] == plan["num_splits"], plan
+    # paged bf16 with Q in LDS: the chunk leaves room for Q beside the tiles and the row table
+    plan = G.gqa_decode_make_plan(base(**kw, kv_dtype="bf16", layout="paged", page_size=16, max_pages_per_seq=8192,
+                                       topk=8192))
+    assert plan["kv_chunk"] * 8 + 4096 + 16384 + 4 * 32768 + 512 <= 160 * 1024, plan
+
+
 def test_plan_forced_chunk_and_single_split():
     p = base(kv_chunk=32)
     plan = G.gqa_decode_make_plan(p)
